@@ -1,0 +1,294 @@
+"""Plain fp64 CPU oracle for decode context parallelism (DCP) on MLA/DSA decode.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The HIP
+library never does, and this module imports nothing from it: the two share no
+code, headers, tables or helpers.  Slow and obviously correct on purpose: every
+function is the plain definition, written out with numpy in float64.
+
+Pages this follows (the text of three public pull-request pages):
+
+  [P1] "feat: support decode context parallelism for PyTorch MLA"
+       (LMDeploy pull request 4952)
+  [P2] "Feat[DCP] Support decode context parallelism for DSA models with the
+       flashmla_kv backend" (SGLang pull request 36990)
+  [P3] "[DSA] Fix decode context parallelism for RoPE sparse attention on
+       Blackwell" (SGLang pull request 42536)
+
+What the path computes, in the pages' terms:
+
+* The KV cache of a sequence is split token by token over N shards with
+  interleave 1: position t lives on shard t mod N ([P1] "Server and client
+  commands", the vLLM run that selected interleave 1 and block size 64).
+* Each shard attends the query heads of the whole DCP group to its own KV only
+  and returns the output together with its log-sum-exp ([P1] Summary, decode
+  bullet; [P3] Motivation, first cause, and Modifications, Backend).
+* For sparse (DSA) attention the global top-k slot table is first turned into
+  this shard's local slot ids, moved to the front of the row, with a count per
+  row ([P3] Modifications, Index remap).
+* The partial results are merged with LSE weights ([P1] Summary); a row with no
+  local KV contributes nothing and the merge returns zero when every shard is
+  empty ([P3] Modifications, Fixes in shared code; [P2] review of the LSE
+  combine, which asks for a zero output and a -inf global LSE in that case).
+
+Readings taken where the pages are silent (all listed in the design notes):
+
+* Key rows have 576 dims (512 latent + 64 RoPE); the value is the first 512
+  dims of the same row (absorbed-weight MLA).
+* A global slot id g names row g div N of shard g mod N's pool (the DCP-wide
+  logical block holds page_size*N tokens; [P1] review note that the scheduler
+  unit becomes block_size*dcp, and [P2] review note that locations span
+  (size + page_size)*dcp).
+* Compaction keeps the original relative order; entries past the count are -1;
+  any negative entry is padding.
+* LSE is the natural log of the sum of exp of the scaled logits; an empty row
+  gives output 0 and LSE -inf.
+* FP8 is OCP E4M3FN (bias 7, no infinities, 0x7F/0xFF are NaN) and the stored
+  value is code * per-token scale, one fp32 scale for all 576 dims of a token.
+* Dense attention of a row reads local tokens j < n_r(b) of its sequence b,
+  found through the block table: row BT[b][j div page] * page + j mod page of
+  the shard's pool.  One query row per sequence (no causal mask is defined).
+"""
+
+import numpy as np
+
+D_K = 576   # key width: 512 latent + 64 RoPE
+D_V = 512   # value width: the latent part of the same row
+
+# E4M3FN: exponent and mantissa all ones is NaN, for either sign.
+E4M3_NAN_CODES = (0x7F, 0xFF)
+
+
+# ---------------------------------------------------------------------------
+# Element decoders (exact in float64)
+# ---------------------------------------------------------------------------
+
+def decode_bf16(bits):
+    """bfloat16 bit patterns (uint16) -> float64, exactly.
+
+    A bfloat16 is the upper half of an IEEE binary32, so the bits shifted left
+    by 16 and read as float32 give the value; widening to float64 is exact.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3fn(codes):
+    """OCP FP8 E4M3FN codes (uint8) -> float64, from the bit definition.
+
+    sign s = bit 7, exponent e = bits 6..3 (bias 7), mantissa m = bits 2..0.
+    e == 0: (-1)^s * m * 2^-9 (subnormal); otherwise (-1)^s * (1 + m/8) * 2^(e-7).
+    Codes 0x7F and 0xFF are NaN; the format has no infinities.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = c >> 7
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    sign = np.where(s == 1, -1.0, 1.0)
+    subnormal = m.astype(np.float64) * 2.0 ** -9
+    normal = (1.0 + m.astype(np.float64) / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    v = sign * np.where(e == 0, subnormal, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+_E4M3_TABLE = decode_e4m3fn(np.arange(256, dtype=np.uint8))
+
+
+def dequant_rows(pool, rows, kv_dtype, scale=None):
+    """Gather pool rows and return their exact float64 values, shape [n, 576].
+
+    kv_dtype "bf16": pool holds bfloat16 bit patterns (uint16) [pool_rows, 576].
+    kv_dtype "fp8":  pool holds E4M3FN codes (uint8) [pool_rows, 576] and
+                     ``scale`` holds one float32 per row; value = code * scale.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    if kv_dtype == "bf16":
+        return decode_bf16(np.asarray(pool)[rows])
+    if kv_dtype == "fp8":
+        codes = np.asarray(pool)[rows]
+        s = np.asarray(scale, dtype=np.float32)[rows].astype(np.float64)
+        return _E4M3_TABLE[codes] * s[:, None]
+    raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# Step 1: index remap ([P3] Modifications, Index remap)
+# ---------------------------------------------------------------------------
+
+def remap_topk(table, num_shards, pool_rows=None):
+    """Global top-k slot table -> per-shard compacted local slot ids and counts.
+
+    For shard r and row i: keep the entries g >= 0 of row i with g mod N == r,
+    in their original order, replace each by g div N, put them at the front of
+    the row and record how many there are.  The rest of the row is -1.
+
+    Returns (local [N, R, k] int32, counts [N, R] int32).
+    Preconditions (asserted): the valid entries of a row are distinct and, when
+    ``pool_rows`` is given, below N * pool_rows.
+    """
+    t = np.asarray(table, dtype=np.int64)
+    rows, k = t.shape
+    n = int(num_shards)
+    assert n >= 1
+    local = np.full((n, rows, k), -1, dtype=np.int32)
+    counts = np.zeros((n, rows), dtype=np.int32)
+    for i in range(rows):
+        valid = t[i][t[i] >= 0]
+        assert np.unique(valid).size == valid.size, "duplicate slot in a top-k row"
+        if pool_rows is not None:
+            assert (valid < n * int(pool_rows)).all(), "slot beyond the pool"
+        for r in range(n):
+            own = valid[valid % n == r] // n
+            local[r, i, : own.size] = own
+            counts[r, i] = own.size
+    return local, counts
+
+
+# ---------------------------------------------------------------------------
+# Step 2: attention with LSE over one shard ([P3] Modifications, Backend;
+# [P1] Summary, decode bullet)
+# ---------------------------------------------------------------------------
+
+def attend(q, keys, sigma):
+    """Softmax attention of H query rows over n key rows, with its LSE.
+
+    q [H, 576], keys [n, 576] (float64).  Logits z = sigma * q . k over all 576
+    dims; values are keys[:, :512].  Returns (O [H, 512], lse [H]) with
+    O = sum_j e^{z_j} v_j / sum_j e^{z_j} and lse = ln sum_j e^{z_j}, computed
+    with the row maximum subtracted.  n == 0 gives O = 0 and lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    h = q.shape[0]
+    if keys.shape[0] == 0:
+        return np.zeros((h, D_V)), np.full(h, -np.inf)
+    z = sigma * (q @ keys.T)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ keys[:, :D_V]) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def sparse_attn_shard(q, pool, kv_dtype, scale, local_table, counts, sigma):
+    """Per-shard sparse attention: row i attends local_table[i, :counts[i]].
+
+    q [R, H, 576] float64; pool/scale as in ``dequant_rows``.
+    Returns (O_r [R, H, 512], lse_r [R, H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    rows, heads, _ = q.shape
+    o = np.zeros((rows, heads, D_V))
+    lse = np.full((rows, heads), -np.inf)
+    for i in range(rows):
+        sel = np.asarray(local_table[i][: int(counts[i])], dtype=np.int64)
+        keys = dequant_rows(pool, sel, kv_dtype, scale)
+        o[i], lse[i] = attend(q[i], keys, sigma)
+    return o, lse
+
+
+def dense_local_rows(block_table_row, n_local, page_size):
+    """Pool rows of local tokens j < n_local: BT[j div page]*page + j mod page."""
+    j = np.arange(int(n_local), dtype=np.int64)
+    pages = np.asarray(block_table_row, dtype=np.int64)[j // page_size]
+    return pages * page_size + j % page_size
+
+
+def dense_attn_shard(q, pool, kv_dtype, scale, block_table, local_len, page_size,
+                     sigma):
+    """Per-shard dense attention: row b attends all its local tokens.
+
+    One query row per sequence; local_len[b] = n_r(b) tokens of sequence b live
+    on this shard, addressed through block_table[b].
+    Returns (O_r [B, H, 512], lse_r [B, H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    rows, heads, _ = q.shape
+    o = np.zeros((rows, heads, D_V))
+    lse = np.full((rows, heads), -np.inf)
+    for b in range(rows):
+        sel = dense_local_rows(block_table[b], local_len[b], page_size)
+        keys = dequant_rows(pool, sel, kv_dtype, scale)
+        o[b], lse[b] = attend(q[b], keys, sigma)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Step 3: LSE-weighted merge ([P1] Summary; [P3] Fixes in shared code;
+# [P2] review of the LSE combine; [P1] review: merge arithmetic in fp32 there,
+# float64 here)
+# ---------------------------------------------------------------------------
+
+def lse_merge(o_parts, lse_parts):
+    """Merge N partial (O_r, lse_r) into (O, lse).
+
+    M = max over shards with lse_r > -inf.  w_r = e^{lse_r - M} for those shards;
+    shards with lse_r = -inf are skipped (their O_r is never read, so garbage
+    or NaN there cannot leak).  O = sum w_r O_r / sum w_r, lse = M + ln sum w_r.
+    If no shard is valid: O = 0 and lse = -inf.
+
+    o_parts [N, R, H, Dv], lse_parts [N, R, H] -> (O [R, H, Dv], lse [R, H]).
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    assert not np.isnan(lse_parts).any(), "NaN LSE in a partial"
+    valid = lse_parts > -np.inf
+    any_valid = valid.any(axis=0)
+    m = np.where(valid, lse_parts, -np.inf).max(axis=0)
+    m_safe = np.where(any_valid, m, 0.0)
+    w = np.where(valid, np.exp(np.where(valid, lse_parts - m_safe, 0.0)), 0.0)
+    w_sum = w.sum(axis=0)
+    contrib = np.where(valid[..., None], o_parts, 0.0) * w[..., None]
+    denom = np.where(any_valid, w_sum, 1.0)
+    o = np.where(any_valid[..., None], contrib.sum(axis=0) / denom[..., None], 0.0)
+    lse = np.where(any_valid, m_safe + np.log(denom), -np.inf)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Unsharded references: one softmax over the union of the selected tokens.
+# DCP reaches exactly this result (up to rounding order).
+# ---------------------------------------------------------------------------
+
+def unsharded_sparse(q, pools, kv_dtype, scales, table, sigma):
+    """Attention of each row over all valid slots of its global top-k row.
+
+    Slot g is row g div N of shard g mod N's pool.  pools/scales are lists of N
+    per-shard arrays (scales entries None for bf16).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n = len(pools)
+    t = np.asarray(table, dtype=np.int64)
+    rows, heads, _ = q.shape
+    o = np.zeros((rows, heads, D_V))
+    lse = np.full((rows, heads), -np.inf)
+    for i in range(rows):
+        g = t[i][t[i] >= 0]
+        keys = np.zeros((g.size, D_K))
+        for r in range(n):
+            on_r = g % n == r
+            keys[on_r] = dequant_rows(pools[r], g[on_r] // n, kv_dtype, scales[r])
+        o[i], lse[i] = attend(q[i], keys, sigma)
+    return o, lse
+
+
+def unsharded_dense(q, pools, kv_dtype, scales, block_table, local_lens, page_size,
+                    sigma):
+    """Attention of each sequence row over the union of every shard's tokens.
+
+    local_lens [N, B]: tokens of sequence b held by shard r (0 = shard empty).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n = len(pools)
+    rows, heads, _ = q.shape
+    o = np.zeros((rows, heads, D_V))
+    lse = np.full((rows, heads), -np.inf)
+    for b in range(rows):
+        parts = [
+            dequant_rows(pools[r], dense_local_rows(block_table[b], local_lens[r][b],
+                                                    page_size), kv_dtype, scales[r])
+            for r in range(n)
+        ]
+        o[b], lse[b] = attend(q[b], np.concatenate(parts, axis=0), sigma)
+    return o, lse
