@@ -1,0 +1,211 @@
+/*
+ * dcp_mla.h -- C ABI of libdcpmla.so: the decode hot path of decode context
+ * parallelism (DCP) for MLA / DSA models, as hand-written HIP for gfx950.
+ *
+ * Pages cited (the text of three public pull-request pages):
+ *   [P1] "feat: support decode context parallelism for PyTorch MLA"
+ *        (LMDeploy pull request 4952)
+ *   [P2] "Feat[DCP] Support decode context parallelism for DSA models with
+ *        the flashmla_kv backend" (SGLang pull request 36990)
+ *   [P3] "[DSA] Fix decode context parallelism for RoPE sparse attention on
+ *        Blackwell" (SGLang pull request 42536)
+ *
+ * The method.  The KV cache of every sequence is split token by token over N
+ * shards with interleave 1: position t lives on shard t mod N ([P1] Server
+ * and client commands, the vLLM run with interleave 1 and block size 64).
+ * Each shard runs the query heads of the whole DCP group over its own tokens
+ * only, returns the output together with its log-sum-exp, and the partials
+ * are merged with LSE weights ([P1] Summary; [P3] Motivation and
+ * Modifications, Backend).  Here the N shards are N cache slices on one GPU.
+ *
+ * Conventions for every entry point.
+ *   - All sizes are element counts; all arrays are row-major and contiguous.
+ *   - Pointers marked "device" are GPU memory; "host" pointers are read
+ *     during the call only.  The caller owns every buffer; the library never
+ *     allocates, frees or synchronises, so the calls may be captured in a
+ *     HIP graph.  Work is queued on `stream` and completes asynchronously.
+ *   - Outputs must not alias inputs.
+ *   - Argument checks run on the host before anything is queued.  On any
+ *     error nothing is launched and nothing is written; the status says why.
+ *     A failed launch is reported as DCP_ERR_LAUNCH.
+ *   - Not checked (undefined if violated): device pointers really point to
+ *     buffers of the stated sizes; table entries are -1 or a valid slot;
+ *     the valid entries of a top-k row are distinct.
+ *   - Key rows have DCP_HEAD_DIM = 576 values (512 latent + 64 RoPE); the
+ *     value of a token is the first DCP_V_DIM = 512 values of its key row
+ *     (absorbed-weight MLA).
+ */
+#ifndef DCP_MLA_H
+#define DCP_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DCP_ABI_VERSION 1
+#define DCP_HEAD_DIM 576
+#define DCP_V_DIM 512
+#define DCP_MAX_SHARDS 16
+
+typedef enum dcp_status {
+  DCP_OK = 0,
+  DCP_ERR_INVALID_ARGUMENT = 1,  /* null pointer, non-positive size, bad index   */
+  DCP_ERR_UNSUPPORTED = 2,       /* valid but not implemented (e.g. heads = 48)  */
+  DCP_ERR_WORKSPACE_TOO_SMALL = 3,
+  DCP_ERR_LAUNCH = 4             /* the HIP runtime rejected a kernel launch     */
+} dcp_status;
+
+typedef enum dcp_kv_dtype {
+  DCP_KV_BF16 = 0,       /* bfloat16 rows, 1152 bytes per token                     */
+  DCP_KV_FP8_E4M3 = 1    /* OCP E4M3FN codes, 576 bytes per token, value =
+                            code * scale with one fp32 scale per token            */
+} dcp_kv_dtype;
+
+typedef enum dcp_out_dtype {
+  DCP_OUT_F32 = 0,       /* merged output stored as float32                      */
+  DCP_OUT_BF16 = 1       /* merged in fp32, stored as bfloat16 ([P1] review of
+                            the prefix merge: fp32 arithmetic, BF16 storage)      */
+} dcp_out_dtype;
+
+/* One shard's paged latent KV cache (device pointers). */
+typedef struct dcp_kv_shard {
+  const void* kv;           /* [pool_rows, 576] bf16, or uint8 E4M3FN codes      */
+  const float* kv_scale;    /* [pool_rows] fp32 per-token scale (FP8); NULL for BF16 */
+  int64_t pool_rows;        /* rows in this shard's pool = physical pages * page  */
+  const int32_t* local_len; /* dense only: [num_seqs] tokens of each sequence held
+                               by this shard (0 = none); NULL for sparse          */
+} dcp_kv_shard;
+
+/* Human-readable name of a status code (static storage). */
+const char* dcp_status_string(dcp_status status);
+
+/* DCP_ABI_VERSION of the built library. */
+int32_t dcp_abi_version(void);
+
+/*
+ * Step 1 -- index remap ([P3] Modifications, Index remap; remapped tables are
+ * reused by the layers that share a top-k, [P3] Modifications, Decode latency).
+ *
+ * For every row i and shard r: keep the entries g >= 0 of topk_global[i] with
+ * g mod N == r, in their original order, write g div N to the front of
+ * topk_local[r][i], fill the rest of that row with -1 and write the number
+ * kept to counts[r][i].  A slot id g names row g div N of shard g mod N's pool
+ * (the DCP-wide logical page holds page * N tokens; [P1] review note that the
+ * scheduling unit becomes block_size * dcp).  Negative entries are padding.
+ *
+ *   topk_global  device int32 [rows, k]
+ *   num_shards   N, 1 <= N <= DCP_MAX_SHARDS
+ *   shard        < 0: all shards, outputs [N, rows, k] and [N, rows];
+ *                0 <= shard < N: that shard only, outputs [1, rows, k], [1, rows]
+ *   topk_local   device int32 output
+ *   counts       device int32 output
+ * Bit-exact and deterministic.
+ */
+dcp_status dcp_remap_topk(const int32_t* topk_global, int64_t rows, int32_t k,
+                          int32_t num_shards, int32_t shard, int32_t* topk_local,
+                          int32_t* counts, hipStream_t stream);
+
+/*
+ * Workspace for the decode entry points.  Pass the same arguments as the
+ * decode call: dense = 0 for mla_sparse_decode_lse (tokens_per_shard = k,
+ * page_size ignored) and dense = 1 for mla_dense_decode_lse
+ * (tokens_per_shard = max_local_len); num_splits as passed to that call
+ * (0 = library default); want_partials / want_merged = whether
+ * (o_part, lse_part) / (o, lse) will be given.  Returns 0 when the call needs
+ * no workspace, and SIZE_MAX for arguments the decode call would reject.
+ * The first bytes hold arrival counters: zero the workspace once after
+ * allocating it; every call leaves the counters zeroed again.  Calls that
+ * share one workspace must be ordered on one stream.
+ */
+size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
+                                 int32_t num_shards, int64_t tokens_per_shard,
+                                 int32_t page_size, int32_t num_splits,
+                                 int32_t want_partials, int32_t want_merged);
+
+/*
+ * Step 2 (+ step 3 fused) -- sparse absorbed-MLA decode with LSE over the
+ * shards' compacted local slots ([P3] Modifications, Backend: attention with
+ * return_lse, rows without local KV fixed up, partials merged; [P3] Follow-ups,
+ * item 1: pack and combine fused into the attention).
+ *
+ * For every row i, head h and shard r with J = topk_local[r][i][0:counts[r][i]]:
+ *   z_j   = softmax_scale * sum_d q[i][h][d] * K_r[j][d]    (d < 576)
+ *   O_r   = sum_j e^{z_j} V_r[j] / sum_j e^{z_j}             (V = K[:, :512])
+ *   LSE_r = ln sum_j e^{z_j};   J empty -> O_r = 0, LSE_r = -inf.
+ * K_r[j] is pool row j of shard r (FP8: code * kv_scale[j]).
+ * Merge over shards ([P1] Summary; [P3] Fixes in shared code; [P2] review of
+ * the LSE combine): M = max_r LSE_r over shards with LSE_r > -inf,
+ *   O = sum_r e^{LSE_r - M} O_r / sum_r e^{LSE_r - M},  LSE = M + ln sum(...),
+ *   and O = 0, LSE = -inf when every shard is empty.
+ *
+ *   q            device bf16 [rows, heads, 576]; heads in {16, 32, 64, 128}
+ *                (the gathered heads of a DCP group, [P3] Motivation)
+ *   shards       host array [num_shards] of device pool descriptors
+ *   topk_local   device int32 [num_shards, rows, k]   (dcp_remap_topk output)
+ *   counts       device int32 [num_shards, rows]
+ *   o_part, lse_part  optional device fp32 [num_shards, rows, heads, 512] and
+ *                [num_shards, rows, heads]: the per-shard partials
+ *   o, lse       optional device [rows, heads, 512] (fp32 or bf16 per out_dtype)
+ *                and fp32 [rows, heads]: the merged result
+ *   At least one of the pairs (o_part, lse_part) / (o, lse) must be given,
+ *   each pair complete.
+ *   num_splits   token splits per (row, shard); 0 = library default
+ *   workspace    device, >= dcp_decode_workspace_size(...) bytes (may be NULL
+ *                when that size is 0)
+ */
+dcp_status mla_sparse_decode_lse(const void* q, int64_t rows, int32_t heads,
+                                 const dcp_kv_shard* shards, int32_t num_shards,
+                                 dcp_kv_dtype kv_dtype, const int32_t* topk_local,
+                                 const int32_t* counts, int32_t k, float softmax_scale,
+                                 float* o_part, float* lse_part, void* o, float* lse,
+                                 dcp_out_dtype out_dtype, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Step 2 (+ step 3 fused) -- dense absorbed-MLA decode with LSE over every
+ * local token of each sequence ([P1] Summary, dense FlashMLA decode with DCP).
+ * One query row per sequence.  Local token j < local_len[b] of shard r is
+ * pool row block_table[b][j / page_size] * page_size + j % page_size: the
+ * block table holds DCP-wide logical pages and each shard stores page_size
+ * tokens of every page ([P1] review note on block_size * dcp).  Otherwise as
+ * mla_sparse_decode_lse; a shard with local_len[b] == 0 contributes nothing.
+ *
+ *   block_table  device int32 [rows, max_pages]
+ *   max_local_len  upper bound of every shards[r].local_len[b]; sizes splits
+ */
+dcp_status mla_dense_decode_lse(const void* q, int64_t rows, int32_t heads,
+                                const dcp_kv_shard* shards, int32_t num_shards,
+                                dcp_kv_dtype kv_dtype, const int32_t* block_table,
+                                int32_t max_pages, int32_t page_size,
+                                int64_t max_local_len, float softmax_scale,
+                                float* o_part, float* lse_part, void* o, float* lse,
+                                dcp_out_dtype out_dtype, int32_t num_splits,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Step 3 standalone -- LSE-weighted merge of partials ([P1] Summary; [P3]
+ * Fixes in shared code: zero when every shard is empty; [P2] review of the
+ * LSE combine: safe denominator, -inf global LSE).  Shards whose LSE is -inf
+ * are skipped, never multiplied by zero, so NaN garbage in their O is ignored.
+ *
+ *   o_part   device fp32 [num_shards, rows, heads, dv]
+ *   lse_part device fp32 [num_shards, rows, heads]
+ *   o        device [rows, heads, dv], fp32 or bf16 per out_dtype
+ *   lse      device fp32 [rows, heads]
+ *   dv       value width, a positive multiple of 4 (512 for MLA)
+ */
+dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_shards,
+                       int64_t rows, int32_t heads, int32_t dv, void* o, float* lse,
+                       dcp_out_dtype out_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_MLA_H */

@@ -1,0 +1,291 @@
+// Host side of the C ABI: argument checks, split and workspace planning, and
+// dispatch to the HIP kernels.  Every check runs before anything is queued, so
+// a rejected call writes nothing.  No allocation, no synchronisation.
+#include <cmath>
+#include <cstring>
+#include <limits>
+
+#include "dcp_internal.h"
+
+namespace dcp {
+
+namespace {
+
+inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool valid_heads(int heads) { return heads == 16 || heads == 32 || heads == 64 || heads == 128; }
+
+// Smallest split count that keeps every block's slot list within its LDS
+// budget (sparse: slot ids; dense: pages).
+long long min_splits_for_list(long long tokens_max, bool dense, int page_size) {
+  long long cap = dense ? (long long)(kMaxList - 2) * page_size : (long long)(kMaxList - 64);
+  if (tokens_max <= 0) return 1;
+  return ceil_div(tokens_max, cap);
+}
+
+dcp_status resolve_splits(long long rows, int num_shards, long long tok_expected,
+                          long long tok_max, bool dense, int page_size, int requested,
+                          int* splits_out) {
+  if (requested < 0) return DCP_ERR_INVALID_ARGUMENT;
+  long long need = min_splits_for_list(tok_max, dense, page_size);
+  long long s = requested > 0 ? requested
+                              : std::max<long long>(need, default_splits(rows, num_shards,
+                                                                        tok_expected, tok_max));
+  if (s < need) return DCP_ERR_UNSUPPORTED;
+  if (s * num_shards > kMaxMergeInputs) return DCP_ERR_UNSUPPORTED;
+  *splits_out = (int)s;
+  return DCP_OK;
+}
+
+// Sparse: a shard holds about k / N of a row's k slots (at most k).
+// Dense: a shard holds up to max_local_len tokens of a sequence.
+dcp_status plan_splits(bool dense, long long rows, int num_shards, long long tokens_per_shard,
+                       int page_size, int requested, int* splits_out) {
+  long long expected = dense ? tokens_per_shard : ceil_div(tokens_per_shard, num_shards);
+  return resolve_splits(rows, num_shards, expected, tokens_per_shard, dense, page_size, requested,
+                        splits_out);
+}
+
+}  // namespace
+
+// Token splits per (row, shard): enough blocks to cover the chip once, at
+// least 128 tokens per split, at most 32K tokens per split.
+int default_splits(long long rows, int num_shards, long long tok_expected, long long tok_max) {
+  (void)tok_max;
+  long long units = std::max<long long>(1, rows * num_shards);
+  long long s = ceil_div(kAssumedCUs, units);
+  s = std::max(s, ceil_div(std::max<long long>(tok_expected, 1), 32768));
+  s = std::min(s, std::max<long long>(1, ceil_div(std::max<long long>(tok_expected, 1), 128)));
+  s = std::min<long long>(s, kMaxMergeInputs / num_shards);
+  return (int)std::max<long long>(1, s);
+}
+
+WorkspacePlan plan_workspace(long long rows, int heads, int num_shards, int splits,
+                             bool want_partials, bool want_merged) {
+  WorkspacePlan w{};
+  w.splits = splits;
+  w.fused = want_merged;
+  w.partials = want_partials;
+  w.needs_block_partials = want_merged || (want_partials && splits > 1);
+  size_t off = 0;
+  w.cnt_row_off = off;
+  if (want_merged) off += sizeof(int) * (size_t)rows;
+  w.cnt_shard_off = off;
+  if (want_partials && splits > 1) off += sizeof(int) * (size_t)rows * num_shards;
+  off = align256(off);
+  w.ws_o_off = off;
+  size_t blocks = (size_t)rows * num_shards * splits;
+  if (w.needs_block_partials) off += sizeof(float) * blocks * heads * kVDim;
+  off = align256(off);
+  w.ws_lse_off = off;
+  if (w.needs_block_partials) off += sizeof(float) * blocks * heads;
+  w.total = (want_merged || (want_partials && splits > 1)) ? align256(off) : 0;
+  return w;
+}
+
+namespace {
+
+dcp_status check_shards(const dcp_kv_shard* shards, int num_shards, dcp_kv_dtype kv_dtype,
+                        bool dense) {
+  if (!shards) return DCP_ERR_INVALID_ARGUMENT;
+  for (int r = 0; r < num_shards; ++r) {
+    const dcp_kv_shard& s = shards[r];
+    if (!s.kv || s.pool_rows < 1) return DCP_ERR_INVALID_ARGUMENT;
+    if (kv_dtype == DCP_KV_FP8_E4M3 && !s.kv_scale) return DCP_ERR_INVALID_ARGUMENT;
+    if (dense && !s.local_len) return DCP_ERR_INVALID_ARGUMENT;
+  }
+  return DCP_OK;
+}
+
+struct CommonArgs {
+  const void* q;
+  long long rows;
+  int heads;
+  const dcp_kv_shard* shards;
+  int num_shards;
+  dcp_kv_dtype kv_dtype;
+  float softmax_scale;
+  float* o_part;
+  float* lse_part;
+  void* o;
+  float* lse;
+  dcp_out_dtype out_dtype;
+  int num_splits;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+dcp_status check_common(const CommonArgs& a, bool dense) {
+  if (a.rows < 0 || a.num_shards < 1 || a.num_shards > kMaxShards) return DCP_ERR_INVALID_ARGUMENT;
+  if (a.kv_dtype != DCP_KV_BF16 && a.kv_dtype != DCP_KV_FP8_E4M3) return DCP_ERR_INVALID_ARGUMENT;
+  if (a.out_dtype != DCP_OUT_F32 && a.out_dtype != DCP_OUT_BF16) return DCP_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(a.softmax_scale)) return DCP_ERR_INVALID_ARGUMENT;
+  if (a.heads < 1 || a.num_splits < 0) return DCP_ERR_INVALID_ARGUMENT;
+  if ((a.o_part == nullptr) != (a.lse_part == nullptr)) return DCP_ERR_INVALID_ARGUMENT;
+  if ((a.o == nullptr) != (a.lse == nullptr)) return DCP_ERR_INVALID_ARGUMENT;
+  if (!a.o_part && !a.o) return DCP_ERR_INVALID_ARGUMENT;
+  if (a.rows == 0) return DCP_OK;
+  if (!a.q) return DCP_ERR_INVALID_ARGUMENT;
+  dcp_status st = check_shards(a.shards, a.num_shards, a.kv_dtype, dense);
+  if (st != DCP_OK) return st;
+  if (!valid_heads(a.heads)) return DCP_ERR_UNSUPPORTED;
+  return DCP_OK;
+}
+
+DecodeParams make_params(const CommonArgs& a, const WorkspacePlan& w) {
+  DecodeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a.q;
+  for (int r = 0; r < a.num_shards; ++r) {
+    p.shard[r].kv = a.shards[r].kv;
+    p.shard[r].scale = a.shards[r].kv_scale;
+    p.shard[r].pool_rows = a.shards[r].pool_rows;
+    p.shard[r].local_len = a.shards[r].local_len;
+  }
+  p.rows = a.rows;
+  p.heads = a.heads;
+  p.num_shards = a.num_shards;
+  p.num_splits = w.splits;
+  p.head_blocks = (a.heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  p.sm_scale_log2 = a.softmax_scale * 1.4426950408889634f;
+  p.o_part = a.o_part;
+  p.lse_part = a.lse_part;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.out_bf16 = a.out_dtype == DCP_OUT_BF16;
+  char* ws = static_cast<char*>(a.workspace);
+  if (w.total > 0) {
+    p.cnt_row = reinterpret_cast<int*>(ws + w.cnt_row_off);
+    p.cnt_shard = reinterpret_cast<int*>(ws + w.cnt_shard_off);
+    p.ws_o = reinterpret_cast<float*>(ws + w.ws_o_off);
+    p.ws_lse = reinterpret_cast<float*>(ws + w.ws_lse_off);
+  }
+  long long blocks = a.rows * a.num_shards * w.splits * p.head_blocks;
+  p.xcd_swizzle = (blocks % 8 == 0) ? 1 : 0;
+  return p;
+}
+
+dcp_status launch_checked(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream) {
+  long long blocks = p.rows * p.num_shards * (long long)p.num_splits * p.head_blocks;
+  if (blocks > 0x7fffffffLL) return DCP_ERR_UNSUPPORTED;
+  return launch_decode(p, fp8, dense, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace dcp
+
+using namespace dcp;
+
+extern "C" {
+
+const char* dcp_status_string(dcp_status status) {
+  switch (status) {
+    case DCP_OK: return "DCP_OK";
+    case DCP_ERR_INVALID_ARGUMENT: return "DCP_ERR_INVALID_ARGUMENT";
+    case DCP_ERR_UNSUPPORTED: return "DCP_ERR_UNSUPPORTED";
+    case DCP_ERR_WORKSPACE_TOO_SMALL: return "DCP_ERR_WORKSPACE_TOO_SMALL";
+    case DCP_ERR_LAUNCH: return "DCP_ERR_LAUNCH";
+  }
+  return "DCP_ERR_UNKNOWN";
+}
+
+int32_t dcp_abi_version(void) { return DCP_ABI_VERSION; }
+
+dcp_status dcp_remap_topk(const int32_t* topk_global, int64_t rows, int32_t k,
+                          int32_t num_shards, int32_t shard, int32_t* topk_local,
+                          int32_t* counts, hipStream_t stream) {
+  if (rows < 0 || k < 0 || num_shards < 1 || num_shards > kMaxShards) return DCP_ERR_INVALID_ARGUMENT;
+  if (shard >= num_shards) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return DCP_OK;
+  if (!counts || (k > 0 && (!topk_global || !topk_local))) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows > 0x7fffffffLL) return DCP_ERR_UNSUPPORTED;
+  return launch_remap(topk_global, rows, k, num_shards, shard, topk_local, counts, stream) == hipSuccess
+             ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
+size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
+                                 int32_t num_shards, int64_t tokens_per_shard,
+                                 int32_t page_size, int32_t num_splits,
+                                 int32_t want_partials, int32_t want_merged) {
+  const size_t bad = std::numeric_limits<size_t>::max();
+  if (rows < 0 || heads < 1 || num_shards < 1 || num_shards > kMaxShards || tokens_per_shard < 0)
+    return bad;
+  if (dense && page_size < 1) return bad;
+  if (!want_partials && !want_merged) return bad;
+  if (rows == 0) return 0;
+  int splits = 0;
+  if (plan_splits(dense != 0, rows, num_shards, tokens_per_shard, page_size, num_splits, &splits) != DCP_OK)
+    return bad;
+  return plan_workspace(rows, heads, num_shards, splits, want_partials != 0, want_merged != 0).total;
+}
+
+dcp_status mla_sparse_decode_lse(const void* q, int64_t rows, int32_t heads,
+                                 const dcp_kv_shard* shards, int32_t num_shards,
+                                 dcp_kv_dtype kv_dtype, const int32_t* topk_local,
+                                 const int32_t* counts, int32_t k, float softmax_scale,
+                                 float* o_part, float* lse_part, void* o, float* lse,
+                                 dcp_out_dtype out_dtype, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  CommonArgs a{q, rows, heads, shards, num_shards, kv_dtype, softmax_scale, o_part, lse_part,
+               o, lse, out_dtype, num_splits, workspace, workspace_bytes};
+  dcp_status st = check_common(a, false);
+  if (st != DCP_OK) return st;
+  if (k < 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return DCP_OK;
+  if (!counts || (k > 0 && !topk_local)) return DCP_ERR_INVALID_ARGUMENT;
+  int splits = 0;
+  st = plan_splits(false, rows, num_shards, k, 1, num_splits, &splits);
+  if (st != DCP_OK) return st;
+  WorkspacePlan w = plan_workspace(rows, heads, num_shards, splits, o_part != nullptr, o != nullptr);
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return DCP_ERR_WORKSPACE_TOO_SMALL;
+  DecodeParams p = make_params(a, w);
+  p.topk_local = topk_local;
+  p.counts = counts;
+  p.k = k;
+  return launch_checked(p, kv_dtype == DCP_KV_FP8_E4M3, false, stream);
+}
+
+dcp_status mla_dense_decode_lse(const void* q, int64_t rows, int32_t heads,
+                                const dcp_kv_shard* shards, int32_t num_shards,
+                                dcp_kv_dtype kv_dtype, const int32_t* block_table,
+                                int32_t max_pages, int32_t page_size,
+                                int64_t max_local_len, float softmax_scale,
+                                float* o_part, float* lse_part, void* o, float* lse,
+                                dcp_out_dtype out_dtype, int32_t num_splits,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  CommonArgs a{q, rows, heads, shards, num_shards, kv_dtype, softmax_scale, o_part, lse_part,
+               o, lse, out_dtype, num_splits, workspace, workspace_bytes};
+  dcp_status st = check_common(a, true);
+  if (st != DCP_OK) return st;
+  if (max_pages < 1 || page_size < 1 || max_local_len < 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (max_local_len > (long long)max_pages * page_size) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return DCP_OK;
+  if (!block_table) return DCP_ERR_INVALID_ARGUMENT;
+  int splits = 0;
+  st = plan_splits(true, rows, num_shards, max_local_len, page_size, num_splits, &splits);
+  if (st != DCP_OK) return st;
+  WorkspacePlan w = plan_workspace(rows, heads, num_shards, splits, o_part != nullptr, o != nullptr);
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return DCP_ERR_WORKSPACE_TOO_SMALL;
+  DecodeParams p = make_params(a, w);
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
+  return launch_checked(p, kv_dtype == DCP_KV_FP8_E4M3, true, stream);
+}
+
+dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_shards,
+                       int64_t rows, int32_t heads, int32_t dv, void* o, float* lse,
+                       dcp_out_dtype out_dtype, hipStream_t stream) {
+  if (num_shards < 1 || rows < 0 || heads < 1 || dv < 4 || dv % 4 != 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (out_dtype != DCP_OUT_F32 && out_dtype != DCP_OUT_BF16) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return DCP_OK;
+  if (!o_part || !lse_part || !o || !lse) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows * heads > 0x7fffffffLL * 4) return DCP_ERR_UNSUPPORTED;
+  return launch_combine(o_part, lse_part, num_shards, rows, heads, dv, o, lse,
+                        out_dtype == DCP_OUT_BF16, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
+}  // extern "C"

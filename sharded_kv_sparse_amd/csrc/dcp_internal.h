@@ -1,0 +1,81 @@
+// Internal declarations shared by the host API (dcp_api.cpp) and the kernel
+// translation units.  Not part of the public ABI (include/dcp_mla.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "dcp_mla.h"
+
+namespace dcp {
+
+constexpr int kHeadDim = DCP_HEAD_DIM;   // 512 latent + 64 RoPE
+constexpr int kVDim = DCP_V_DIM;         // values = first 512 dims of the key row
+constexpr int kMaxShards = DCP_MAX_SHARDS;
+constexpr int kHeadsPerBlock = 64;       // heads one decode block handles
+constexpr int kMaxList = 4096;           // slot ids / pages a decode block stages in LDS
+constexpr int kMaxMergeInputs = 64;      // partials one merge may combine (N * splits)
+constexpr int kAssumedCUs = 256;         // MI355X compute units (split heuristic only)
+
+struct ShardArg {
+  const void* kv;
+  const float* scale;
+  long long pool_rows;
+  const int* local_len;
+};
+
+struct DecodeParams {
+  const void* q;                 // bf16 [rows, heads, 576]
+  ShardArg shard[kMaxShards];
+  long long rows;
+  int heads;                     // total gathered heads
+  int num_shards;
+  int num_splits;
+  int head_blocks;               // heads / 64 rounded up (1 for heads <= 64)
+  float sm_scale_log2;           // softmax_scale * log2(e)
+  // sparse
+  const int* topk_local;         // [N, rows, k]
+  const int* counts;             // [N, rows]
+  int k;
+  // dense
+  const int* block_table;        // [rows, max_pages]
+  int max_pages;
+  int page_size;
+  // outputs
+  float* o_part;                 // [N, rows, heads, 512] or null
+  float* lse_part;               // [N, rows, heads] or null
+  void* o;                       // [rows, heads, 512] fp32 / bf16, or null
+  float* lse;                    // [rows, heads] or null
+  int out_bf16;
+  // workspace
+  float* ws_o;                   // [rows, N, S, heads, 512]
+  float* ws_lse;                 // [rows, N, S, heads]
+  int* cnt_row;                  // [rows]
+  int* cnt_shard;                // [rows, N]
+  int xcd_swizzle;               // grid is a multiple of 8: keep a row's blocks on one XCD
+};
+
+// Workspace plan shared by the size query and the decode calls.
+struct WorkspacePlan {
+  int splits;
+  bool fused;
+  bool partials;
+  bool needs_block_partials;     // blocks write split partials to the workspace
+  size_t cnt_row_off, cnt_shard_off, ws_o_off, ws_lse_off, total;
+};
+
+int default_splits(long long rows, int num_shards, long long tokens_per_shard_expected,
+                   long long tokens_per_shard_max);
+WorkspacePlan plan_workspace(long long rows, int heads, int num_shards, int splits,
+                             bool want_partials, bool want_merged);
+
+// Kernel launchers (return the hipError_t of the launch).
+hipError_t launch_remap(const int* topk_global, long long rows, int k, int num_shards,
+                        int shard, int* topk_local, int* counts, hipStream_t stream);
+hipError_t launch_combine(const float* o_part, const float* lse_part, int num_shards,
+                          long long rows, int heads, int dv, void* o, float* lse,
+                          int out_bf16, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream);
+
+}  // namespace dcp

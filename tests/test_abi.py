@@ -1,0 +1,157 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before queuing work.
+No call here reaches a kernel launch (every case fails validation first or is
+a documented no-op)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sharded_kv_sparse_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcp_mla.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from sharded_kv_sparse_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "defined")))
+
+
+def test_header_declares_the_binding_exports():
+    assert sorted(B.EXPORTS) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.dcp_abi_version() == 1
+    for code, name in B.STATUS_NAMES.items():
+        assert L.dcp_status_string(code).decode() == name
+    assert L.dcp_status_string(99).decode() == "DCP_ERR_UNKNOWN"
+
+
+def test_remap_argument_checks(L):
+    f = L.dcp_remap_topk
+    assert f(None, 4, 16, 2, -1, FAKE, FAKE, None) == INVALID          # null input
+    assert f(FAKE, 4, 16, 2, -1, None, FAKE, None) == INVALID          # null output
+    assert f(FAKE, 4, 16, 2, -1, FAKE, None, None) == INVALID          # null counts
+    assert f(FAKE, 4, 16, 0, -1, FAKE, FAKE, None) == INVALID          # N < 1
+    assert f(FAKE, 4, 16, 17, -1, FAKE, FAKE, None) == INVALID         # N > 16
+    assert f(FAKE, 4, 16, 4, 4, FAKE, FAKE, None) == INVALID           # shard >= N
+    assert f(FAKE, -1, 16, 4, -1, FAKE, FAKE, None) == INVALID         # rows < 0
+    assert f(FAKE, 4, -3, 4, -1, FAKE, FAKE, None) == INVALID          # k < 0
+    assert f(None, 0, 16, 4, -1, None, None, None) == OK               # empty: no-op
+
+
+def _shards(n, fp8=False, dense=False, pool_rows=1024):
+    arr = (B.KvShard * n)()
+    for r in range(n):
+        arr[r] = B.KvShard(0x20000, 0x30000 if fp8 else None, pool_rows, 0x40000 if dense else None)
+    return arr
+
+
+def _sparse(L, **kw):
+    a = dict(q=FAKE, rows=4, heads=64, shards=_shards(2), n=2, kv=B.KV_BF16, local=FAKE,
+             counts=FAKE, k=64, scale=0.07, o_part=None, lse_part=None, o=FAKE, lse=FAKE,
+             out=B.OUT_F32, splits=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.mla_sparse_decode_lse(a["q"], a["rows"], a["heads"], a["shards"], a["n"], a["kv"],
+                                   a["local"], a["counts"], a["k"], a["scale"], a["o_part"],
+                                   a["lse_part"], a["o"], a["lse"], a["out"], a["splits"], a["ws"],
+                                   a["ws_bytes"], None)
+
+
+def test_sparse_decode_argument_checks(L):
+    assert _sparse(L, q=None) == INVALID
+    assert _sparse(L, heads=48) == UNSUPPORTED
+    assert _sparse(L, heads=256) == UNSUPPORTED
+    assert _sparse(L, n=0) == INVALID
+    assert _sparse(L, n=17) == INVALID
+    assert _sparse(L, kv=7) == INVALID
+    assert _sparse(L, out=5) == INVALID
+    assert _sparse(L, k=-1) == INVALID
+    assert _sparse(L, counts=None) == INVALID
+    assert _sparse(L, o=None, lse=None) == INVALID                 # no output at all
+    assert _sparse(L, o=None) == INVALID                           # half a pair
+    assert _sparse(L, o_part=FAKE) == INVALID
+    assert _sparse(L, scale=float("nan")) == INVALID
+    assert _sparse(L, scale=float("inf")) == INVALID
+    assert _sparse(L, splits=-2) == INVALID
+    assert _sparse(L, splits=40) == UNSUPPORTED                    # 2 shards x 40 > 64 partials
+    assert _sparse(L, kv=B.KV_FP8_E4M3) == INVALID                 # FP8 needs scales
+    assert _sparse(L, shards=_shards(2, pool_rows=0)) == INVALID
+    assert _sparse(L, ws=None, ws_bytes=0) == WS_SMALL             # merged output needs counters
+    assert _sparse(L, ws_bytes=16) == WS_SMALL
+    assert _sparse(L, rows=0, q=None, shards=None, local=None, counts=None) == OK
+
+
+def test_dense_decode_argument_checks(L):
+    def dense(**kw):
+        a = dict(q=FAKE, rows=2, heads=64, shards=_shards(2, dense=True), n=2, kv=B.KV_BF16,
+                 bt=FAKE, max_pages=8, page=64, max_len=400, scale=0.07, o=FAKE, lse=FAKE,
+                 ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.mla_dense_decode_lse(a["q"], a["rows"], a["heads"], a["shards"], a["n"], a["kv"],
+                                      a["bt"], a["max_pages"], a["page"], a["max_len"], a["scale"],
+                                      None, None, a["o"], a["lse"], B.OUT_F32, 0, a["ws"],
+                                      a["ws_bytes"], None)
+    assert dense(shards=_shards(2, dense=False)) == INVALID        # local_len required
+    assert dense(bt=None) == INVALID
+    assert dense(page=0) == INVALID
+    assert dense(max_pages=0) == INVALID
+    assert dense(max_len=-1) == INVALID
+    assert dense(max_len=8 * 64 + 1) == INVALID                    # beyond the block table
+    assert dense(heads=24) == UNSUPPORTED
+
+
+def test_combine_argument_checks(L):
+    f = L.lse_combine
+    assert f(None, FAKE, 2, 4, 16, 512, FAKE, FAKE, 0, None) == INVALID
+    assert f(FAKE, FAKE, 0, 4, 16, 512, FAKE, FAKE, 0, None) == INVALID
+    assert f(FAKE, FAKE, 2, 4, 16, 6, FAKE, FAKE, 0, None) == INVALID   # dv % 4
+    assert f(FAKE, FAKE, 2, 4, 0, 512, FAKE, FAKE, 0, None) == INVALID
+    assert f(FAKE, FAKE, 2, 4, 16, 512, FAKE, FAKE, 3, None) == INVALID
+    assert f(None, None, 2, 0, 16, 512, None, None, 0, None) == OK      # empty: no-op
+
+
+def test_workspace_size_rules(L):
+    bad = ctypes.c_size_t(-1).value
+    ws = lambda *a: L.dcp_decode_workspace_size(*a)                    # noqa: E731
+    # (dense, rows, heads, shards, tokens, page, splits, partials, merged)
+    assert ws(0, 4, 64, 2, 64, 1, 0, 0, 0) == bad                      # no output requested
+    assert ws(0, 4, 64, 0, 64, 1, 0, 0, 1) == bad
+    assert ws(0, -1, 64, 2, 64, 1, 0, 0, 1) == bad
+    assert ws(1, 4, 64, 2, 64, 0, 0, 0, 1) == bad                      # dense needs a page size
+    assert ws(0, 0, 64, 2, 64, 1, 0, 0, 1) == 0
+    assert ws(0, 64, 64, 4, 2048, 1, 1, 1, 0) == 0                     # partials, one split: none
+    fused = ws(0, 64, 64, 4, 2048, 1, 1, 0, 1)
+    # counters + one fp32 partial (O and LSE) per (row, shard, split, head)
+    assert fused >= 64 * 4 * 64 * (512 + 1) * 4
+    assert ws(0, 64, 64, 4, 2048, 1, 2, 0, 1) > fused                  # more splits, more partials
+    assert ws(0, 128, 64, 4, 2048, 1, 1, 0, 1) > fused
+    assert ws(0, 64, 64, 4, 2048, 1, 2, 1, 1) >= ws(0, 64, 64, 4, 2048, 1, 2, 0, 1)
+
+
+def test_binding_refuses_without_gpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        B.remap_topk(torch.zeros((2, 4), dtype=torch.int32), 2)

@@ -1,0 +1,296 @@
+"""GPU parity of the HIP path against the CPU fp64 oracle, through the C ABI.
+
+Remap: bit-exact.  Attention partials and the merged result: max |dO| <= 1e-2,
+max |dLSE| <= 1e-3 (fp32 outputs), -inf matched exactly, no NaN.  Sizes span
+several tiles with ragged tails; full-size workloads are checked whole (sparse)
+or on sampled rows and heads (the million-token dense shard).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sharded_kv_sparse_amd import binding as B
+from sharded_kv_sparse_amd import workloads as wl
+
+from ._support import (assert_attn_close, check_against_oracle, gpu_dense, gpu_sparse, host_inputs,
+                       make, oracle_dense, oracle_sparse, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------- remap
+
+def test_remap_bit_exact_small_exhaustive(gpu):
+    rng = np.random.default_rng(0)
+    for n in (1, 2, 3, 4, 7, 16):
+        for k in (1, 2, 5, 63, 64, 65, 300, 2048):
+            rows = 5
+            table = rng.integers(-1, 4 * n * 64, size=(rows, k)).astype(np.int32)
+            for i in range(rows):          # make valid entries distinct
+                seen = set()
+                for j in range(k):
+                    if table[i, j] >= 0 and table[i, j] in seen:
+                        table[i, j] = -1
+                    seen.add(int(table[i, j]))
+            table[rows - 1] = -1           # an all-padding row
+            say(f"remap n={n} k={k}")
+            ref_local, ref_counts = oracle.remap_topk(table, n)
+            local, counts = B.remap_topk(torch.from_numpy(table).to(gpu), n)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(local.cpu().numpy(), ref_local)
+            np.testing.assert_array_equal(counts.cpu().numpy(), ref_counts)
+            for s in (0, n - 1):
+                l1, c1 = B.remap_topk(torch.from_numpy(table).to(gpu), n, shard=s)
+                np.testing.assert_array_equal(l1.cpu().numpy()[0], ref_local[s])
+                np.testing.assert_array_equal(c1.cpu().numpy()[0], ref_counts[s])
+
+
+@pytest.mark.parametrize("name", ["sparse_bf16_b8_k2048", "sparse_fp8_b64_k2048",
+                                  "mtp_sparse_bf16_b16x6_k2048"])
+def test_remap_bit_exact_workload_tables(gpu, name):
+    p = wl.preset(name)
+    rng = np.random.default_rng(p.seed)
+    table = wl.make_topk_table(p, wl.make_block_table(p, rng), rng)
+    say(f"remap {name}")
+    ref_local, ref_counts = oracle.remap_topk(table, p.num_shards, p.pool_rows)
+    t = torch.from_numpy(table).to(gpu)
+    first = None
+    for rep in range(3):               # repeat launches are bit-identical
+        local, counts = B.remap_topk(t, p.num_shards)
+        torch.cuda.synchronize()
+        got = (local.cpu().numpy(), counts.cpu().numpy())
+        np.testing.assert_array_equal(got[0], ref_local)
+        np.testing.assert_array_equal(got[1], ref_counts)
+        if first is not None:
+            assert all((a == b).all() for a, b in zip(first, got))
+        first = got
+
+
+def test_remap_empty_rows_and_k_zero(gpu):
+    say("remap rows=0 / k=0")
+    t0 = torch.empty((0, 16), dtype=torch.int32, device=gpu)
+    local, counts = B.remap_topk(t0, 4)
+    assert local.shape == (4, 0, 16)
+    t1 = torch.empty((3, 0), dtype=torch.int32, device=gpu)
+    local, counts = B.remap_topk(t1, 2)
+    torch.cuda.synchronize()
+    assert (counts.cpu().numpy() == 0).all()
+
+
+# ---------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("n,dv", [(1, 512), (2, 512), (4, 512), (8, 64), (5, 4)])
+def test_lse_combine_matches_oracle(gpu, n, dv):
+    rng = np.random.default_rng(n * 100 + dv)
+    rows, heads = 7, 16
+    o_parts = rng.standard_normal((n, rows, heads, dv)).astype(np.float32)
+    lse_parts = (3 * rng.standard_normal((n, rows, heads))).astype(np.float32)
+    lse_parts[:, 0, 0] = -np.inf                         # every shard empty
+    if n > 1:
+        lse_parts[1:, 1, :] = -np.inf                    # only shard 0 present
+        lse_parts[0, 2, 3] = -np.inf                     # shard 0 empty
+    o_parts[lse_parts == -np.inf] = np.nan               # garbage must never leak
+    say(f"combine n={n} dv={dv}")
+    o_ref, lse_ref = oracle.lse_merge(o_parts.astype(np.float64), lse_parts.astype(np.float64))
+    for out_dtype in (B.OUT_F32, B.OUT_BF16):
+        o, lse = B.lse_combine(torch.from_numpy(o_parts).to(gpu), torch.from_numpy(lse_parts).to(gpu),
+                               out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        rel = 2.0 ** -8 if out_dtype == B.OUT_BF16 else 0.0
+        assert_attn_close(to_np(o), to_np(lse), o_ref, lse_ref, f"combine n={n}", o_tol=1e-5,
+                          lse_tol=1e-5, o_rel=rel)
+
+
+# ---------------------------------------------------------------- sparse decode
+
+SPARSE_SMALL = [
+    # (kv, heads, shards, topk, context, pad, rows)
+    ("bf16", 64, 4, 300, 5000, 7, 3),
+    ("fp8", 64, 4, 300, 5000, 7, 3),
+    ("fp8", 32, 2, 257, 3000, 0, 4),
+    ("bf16", 32, 2, 257, 3000, 0, 4),
+    ("fp8", 16, 3, 130, 2000, 3, 2),
+    ("bf16", 16, 1, 200, 2000, 0, 2),
+    ("fp8", 128, 2, 190, 4000, 11, 2),
+    ("bf16", 128, 4, 190, 4000, 0, 2),
+]
+
+
+@pytest.mark.parametrize("kv,heads,n,k,ctx,pad,rows", SPARSE_SMALL)
+def test_sparse_decode_small(gpu, kv, heads, n, k, ctx, pad, rows):
+    p = wl.Preset("t", "sparse", kv, batch=rows, q_per_seq=1, heads=heads, context=ctx,
+                  num_shards=n, topk=k, pad_tail=pad, seed=heads * 7 + n * 3 + k)
+    w = make(p)
+    say(f"sparse small {kv} H={heads} N={n} k={k}")
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    ref = oracle_sparse(w)
+    np.testing.assert_array_equal(res["counts"].cpu().numpy(), ref["counts"])
+    check_against_oracle(res, ref, f"sparse {kv} H={heads} N={n}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [1, 2, 3, 5])
+def test_sparse_decode_splits(gpu, kv, splits):
+    p = wl.Preset("t", "sparse", kv, batch=3, q_per_seq=1, heads=64, context=6000, num_shards=2,
+                  topk=700, pad_tail=5, seed=splits)
+    w = make(p)
+    say(f"sparse splits={splits} {kv}")
+    res = gpu_sparse(w, num_splits=splits)
+    torch.cuda.synchronize()
+    check_against_oracle(res, oracle_sparse(w), f"splits={splits}")
+
+
+@pytest.mark.parametrize("kv,heads", [("fp8", 64), ("fp8", 128), ("bf16", 64), ("bf16", 32)])
+def test_sparse_decode_short_rows(gpu, kv, heads):
+    """Rows with 1..16 selected slots and many heads (a case another stack's
+    sparse kernel got wrong for short FP8 rows with more than 32 heads)."""
+    p = wl.Preset("t", "sparse", kv, batch=6, q_per_seq=1, heads=heads, context=4000,
+                  num_shards=4, topk=64, short_rows=16, seed=heads + 1)
+    w = make(p)
+    say(f"sparse short rows {kv} H={heads}")
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    ref = oracle_sparse(w)
+    assert (ref["counts"] == 0).any()          # some shard owns nothing on some row
+    check_against_oracle(res, ref, f"short rows {kv} H={heads}")
+
+
+def test_sparse_all_empty_rows(gpu):
+    p = wl.Preset("t", "sparse", "fp8", batch=3, q_per_seq=1, heads=64, context=1000,
+                  num_shards=2, topk=32, pad_tail=32, seed=3)
+    w = make(p)
+    say("sparse all-empty")
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    assert (to_np(res["o"]) == 0).all() and (to_np(res["lse"]) == -np.inf).all()
+    assert (to_np(res["o_part"]) == 0).all()
+
+
+@pytest.mark.parametrize("name", ["sparse_bf16_b8_k2048", "sparse_fp8_b64_k2048",
+                                  "mtp_sparse_bf16_b16x6_k2048"])
+def test_sparse_decode_full_workload(gpu, name):
+    p = wl.preset(name)
+    say(f"sparse full {name}: generating")
+    w = make(p)
+    say(f"sparse full {name}: gpu")
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    say(f"sparse full {name}: oracle")
+    ref = oracle_sparse(w)
+    np.testing.assert_array_equal(res["local"].cpu().numpy(), ref["local"])
+    np.testing.assert_array_equal(res["counts"].cpu().numpy(), ref["counts"])
+    err = check_against_oracle(res, ref, name)
+    say(f"{name}: {err}")
+
+
+def test_fused_equals_unfused_and_counters_reset(gpu):
+    p = wl.preset("sparse_fp8_b64_k2048", batch=8, context=16384)
+    w = make(p)
+    say("fused vs unfused")
+    table = w.dev(w.table)
+    local, counts = B.remap_topk(table, p.num_shards)
+    nb = B.workspace_size(False, p.rows, p.heads, p.num_shards, p.topk, want_merged=True,
+                          want_partials=False, num_splits=2)
+    ws = B.alloc_workspace(nb, gpu)
+    a = B.sparse_decode(w.q, w.pools[0], w.scales[0], local, counts, p.sigma, num_splits=2,
+                        workspace=ws)
+    b = B.sparse_decode(w.q, w.pools[0], w.scales[0], local, counts, p.sigma, num_splits=2,
+                        workspace=ws)                       # counters must have reset
+    parts = B.sparse_decode(w.q, w.pools[0], w.scales[0], local, counts, p.sigma, num_splits=2,
+                            want_partials=True, want_merged=False)
+    o_c, lse_c = B.lse_combine(parts["o_part"], parts["lse_part"])
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+    assert (ws[: 4 * p.rows].view(torch.int32) == 0).all()
+    np.testing.assert_allclose(to_np(a["o"]), to_np(o_c), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(to_np(a["lse"]), to_np(lse_c), rtol=0, atol=1e-5)
+    check_against_oracle(a, oracle_sparse(w), "fused")
+
+
+def test_bf16_output(gpu):
+    p = wl.Preset("t", "sparse", "fp8", batch=4, q_per_seq=1, heads=64, context=8000,
+                  num_shards=4, topk=512, seed=11)
+    w = make(p)
+    say("bf16 output")
+    res = gpu_sparse(w, want_partials=False, out_dtype=B.OUT_BF16)
+    torch.cuda.synchronize()
+    assert res["o"].dtype == torch.bfloat16
+    check_against_oracle(res, oracle_sparse(w), "bf16 out")
+
+
+# ---------------------------------------------------------------- dense decode
+
+DENSE_SMALL = [
+    # (kv, heads, shards, context, page, rows, forced_empty)
+    ("bf16", 16, 2, 256, 64, 1, False),
+    ("fp8", 64, 4, 3001, 64, 3, False),
+    ("bf16", 64, 3, 2500, 16, 2, True),
+    ("fp8", 128, 8, 5000, 64, 4, True),
+    ("fp8", 32, 2, 777, 128, 3, False),
+    ("bf16", 32, 1, 1000, 64, 2, False),
+]
+
+
+@pytest.mark.parametrize("kv,heads,n,ctx,page,rows,empty", DENSE_SMALL)
+def test_dense_decode_small(gpu, kv, heads, n, ctx, page, rows, empty):
+    p = wl.Preset("t", "dense", kv, batch=rows, q_per_seq=1, heads=heads, context=ctx,
+                  num_shards=n, page_size=page, forced_empty=empty, seed=ctx + heads)
+    w = make(p)
+    say(f"dense small {kv} H={heads} N={n} ctx={ctx} page={page}")
+    res = gpu_dense(w)
+    torch.cuda.synchronize()
+    check_against_oracle(res, oracle_dense(w), f"dense {kv} H={heads} N={n}")
+
+
+def test_dense_tiny_workload(gpu):
+    w = make(wl.preset("tiny_dense_bf16_ctx256"))
+    say("dense tiny preset")
+    res = gpu_dense(w)
+    torch.cuda.synchronize()
+    ref = oracle_dense(w)
+    check_against_oracle(res, ref, "tiny dense")
+    q, pools, scales = host_inputs(w)
+    o_u, lse_u = oracle.unsharded_dense(q, pools, "bf16", scales, w.block_table, w.local_lens,
+                                        w.p.page_size, w.p.sigma)
+    assert_attn_close(to_np(res["o"]), to_np(res["lse"]), o_u, lse_u, "tiny dense vs unsharded")
+
+
+def test_dense_equals_sparse_on_gpu(gpu):
+    """Dense over every local token == sparse with a table listing them all."""
+    p = wl.Preset("t", "dense", "fp8", batch=2, q_per_seq=1, heads=64, context=1500,
+                  num_shards=2, seed=5)
+    w = make(p)
+    say("dense == sparse")
+    dres = gpu_dense(w, want_partials=True)
+    table = np.stack([wl.positions_to_slots(p, w.block_table, b, np.arange(p.context))
+                      for b in range(p.batch)]).astype(np.int32)
+    local, counts = B.remap_topk(torch.from_numpy(table).to(gpu), p.num_shards)
+    sres = B.sparse_decode(w.q, w.pools[0], w.scales[0], local, counts, p.sigma,
+                           want_partials=True)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(dres["lse"]), to_np(sres["lse"]), rtol=0, atol=1e-4)
+    np.testing.assert_allclose(to_np(dres["o"]), to_np(sres["o"]), rtol=0, atol=2e-3)
+
+
+def test_dense_million_token_sampled(gpu):
+    p = wl.preset("dense_fp8_b32_ctx1m")
+    say("dense 1M: generating")
+    w = make(p)
+    say("dense 1M: gpu")
+    res = gpu_dense(w, want_partials=False)
+    torch.cuda.synchronize()
+    rows = [0, 1, 4, 31]                    # rows 0 and 4 have a forced-empty shard
+    heads = list(range(0, 8)) + list(range(120, 128))
+    say("dense 1M: host copies")
+    host = host_inputs(w)
+    say("dense 1M: oracle on sampled rows/heads")
+    ref = oracle_dense(w, rows=rows, heads=heads, host=host)
+    err = check_against_oracle(res, ref, "dense 1M", rows=rows, heads=heads)
+    say(f"dense 1M: {err}")
