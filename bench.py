@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the DCP decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the index remap of a
+top-k table shared by four consecutive layers, then the fused sparse MLA
+decode (all shards + LSE merge) for each of those four layers, each layer with
+its own KV cache.  The reported value is microseconds per layer-step
+(= step time / 4).  Layers rotate over 16 distinct KV caches (4 table groups x
+4 layers, 1.2 GB touched per cycle) so the 256 MB last-level cache cannot hold
+a layer between its uses: the KV is read from HBM.
+
+Output: one JSON line (rank 0), plus a roofline figure for the decode kernel
+(algorithmic bytes per launch / average launch time from HIP events recorded
+on the launch stream) and the CPU fp64 oracle timed on the host as a baseline.
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+from sharded_kv_sparse_amd import binding as B
+from sharded_kv_sparse_amd import workloads as wl
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16
+METRIC = "µs/layer-step and KV HBM GB/s (% of peak), sparse MLA decode B=64 top-k 2048"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sparse_fp8_b64_k2048", choices=sorted(wl.PRESETS))
+    ap.add_argument("--groups", type=int, default=4, help="table groups (4 layers each) rotated")
+    ap.add_argument("--layers-per-table", type=int, default=4)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the CPU-baseline sample (0 = all rows of one layer-step)")
+    ap.add_argument("--out", default="", help="also write the JSON line to this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: each launch reads and writes exactly 1 GiB."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}))
+
+
+def algorithmic_bytes(w, layer_counts):
+    """Bytes a decode launch must move: KV rows read once, query, slot ids,
+    counts, merged output and LSE."""
+    p = w.p
+    per_token = 580 if p.kv_dtype == "fp8" else 1152
+    kv = int(layer_counts) * per_token
+    q = p.rows * p.heads * 576 * 2
+    out = p.rows * p.heads * (512 * 4 + 4)
+    ids = int(layer_counts) * 4 + p.num_shards * p.rows * 4 if p.kind == "sparse" else 0
+    return kv, kv + q + out + ids
+
+
+def flops(p, tokens):
+    return 2.0 * p.heads * tokens * (576 + 512)
+
+
+def cpu_baseline(w, host, rows):
+    """Time the CPU oracle on one layer-step (or a row sample of it)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    p = w.p
+    q, pools, scales = host
+    sel = np.arange(p.rows) if rows <= 0 else np.arange(min(rows, p.rows))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        if p.kind == "sparse":
+            local, counts = oracle.remap_topk(w.table[sel], p.num_shards, p.pool_rows)
+            parts = [oracle.sparse_attn_shard(q[sel], pools[r], p.kv_dtype, scales[r], local[r],
+                                              counts[r], p.sigma) for r in range(p.num_shards)]
+        else:
+            parts = [oracle.dense_attn_shard(q[sel], pools[r], p.kv_dtype, scales[r],
+                                             w.block_table[sel], w.local_lens[r][sel],
+                                             p.page_size, p.sigma) for r in range(p.num_shards)]
+        oracle.lse_merge(np.stack([a for a, _ in parts]), np.stack([b for _, b in parts]))
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times) * (p.rows / len(sel))
+    import platform
+    return {"value": round(t * 1e6, 1), "unit": "us/layer-step", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"{'all' if len(sel) == p.rows else len(sel)} of {p.rows} rows of one "
+                       f"layer-step (remap + {p.num_shards} shard attentions + merge, fp64 numpy), "
+                       f"median of 3, scaled to {p.rows} rows; host {platform.processor() or 'cpu'}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the DCP shards are cache slices on one device and "
+              "this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    dev = torch.device("cuda:0")
+    p = wl.preset(args.workload)
+    sparse = p.kind == "sparse"
+    lpt = args.layers_per_table if sparse else 1
+    n_layers = args.groups * lpt
+    print(f"[bench] workload {p.name}: generating {n_layers} layer caches", file=sys.stderr, flush=True)
+    groups = []
+    for gi in range(args.groups):
+        w = wl.make_workload(p, device=dev, layers=lpt, seed=p.seed + 1000 * gi)
+        groups.append(w)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    # Per-group device inputs and preallocated outputs / workspace.
+    ws_bytes = B.workspace_size(not sparse, p.rows, p.heads, p.num_shards,
+                                p.topk if sparse else int(groups[0].local_lens.max()),
+                                p.page_size, args.num_splits, want_partials=False, want_merged=True)
+    ws = B.alloc_workspace(ws_bytes, dev)
+    o = torch.empty((p.rows, p.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((p.rows, p.heads), dtype=torch.float32, device=dev)
+    outs = {"o": o, "lse": lse}
+    # Every call is marshalled once up front, so the timed loop is one ctypes
+    # call per launch and the host stays ahead of the GPU.
+    prep = []
+    for w in groups:
+        d = {}
+        if sparse:
+            table = w.dev(w.table)
+            local = torch.empty((p.num_shards, p.rows, p.topk), dtype=torch.int32, device=dev)
+            counts = torch.empty((p.num_shards, p.rows), dtype=torch.int32, device=dev)
+            d["remap"] = B.prepare_remap_topk(table, p.num_shards, out=local, counts=counts,
+                                              stream=stream)
+            d["dec"] = [B.prepare_sparse_decode(w.q, w.pools[li], w.scales[li], local, counts,
+                                                p.sigma, num_splits=args.num_splits, workspace=ws,
+                                                out=outs, stream=stream) for li in range(lpt)]
+        else:
+            bt = w.dev(w.block_table)
+            lens = [w.dev(w.local_lens[r]) for r in range(p.num_shards)]
+            d["dec"] = [B.prepare_dense_decode(w.q, w.pools[li], w.scales[li], bt, lens,
+                                               p.page_size, int(w.local_lens.max()), p.sigma,
+                                               num_splits=args.num_splits, workspace=ws, out=outs,
+                                               stream=stream) for li in range(lpt)]
+        prep.append(d)
+
+    def step(gi, ev=None):
+        d = prep[gi]
+        if sparse:
+            if ev is not None:
+                ev["remap"][0].record(stream)
+            d["remap"]()
+            if ev is not None:
+                ev["remap"][1].record(stream)
+        for li in range(lpt):
+            if ev is not None:
+                ev["dec"][li][0].record(stream)
+            d["dec"][li]()
+            if ev is not None:
+                ev["dec"][li][1].record(stream)
+
+    for s in range(args.warmup):
+        step(s % args.groups)
+    torch.cuda.synchronize()
+
+    def mk():
+        return torch.cuda.Event(enable_timing=True)
+    evs = [{"remap": (mk(), mk()), "dec": [(mk(), mk()) for _ in range(lpt)]}
+           for _ in range(args.steps)]
+    t_start, t_end = mk(), mk()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(s % args.groups, evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    us_per_layer_step = ms_per_step * 1000.0 / lpt
+    dec_us = [e["dec"][li][0].elapsed_time(e["dec"][li][1]) * 1000.0 for e in evs for li in range(lpt)]
+    remap_us = [e["remap"][0].elapsed_time(e["remap"][1]) * 1000.0 for e in evs] if sparse else [0.0]
+
+    # algorithmic bytes / flops of one decode launch (average over the groups)
+    if sparse:
+        valid = [int((w.table >= 0).sum()) for w in groups]
+    else:
+        valid = [int(w.local_lens.sum()) for w in groups]
+    kv_b, tot_b = zip(*[algorithmic_bytes(w, v) for w, v in zip(groups, valid)])
+    kv_b, tot_b, tok = statistics.mean(kv_b), statistics.mean(tot_b), statistics.mean(valid)
+    dec_mean = statistics.mean(dec_us)
+    fl = flops(p, tok)
+    kv_gbps = kv_b / (us_per_layer_step * 1e-6) / 1e9
+    mfma_bound = (fl / (BF16_MFMA_PEAK_TFLOPS * 1e12)) > (tot_b / (HBM_PEAK_GBPS * 1e9))
+    if mfma_bound:
+        achieved = fl / (dec_mean * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = tot_b / (dec_mean * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    roof.update({"kernel": "decode_kernel (fused sparse MLA decode + LSE merge)" if sparse
+                 else "decode_kernel (fused dense MLA decode + LSE merge)",
+                 "avg_launch_us": round(dec_mean, 2), "algorithmic_bytes_per_launch": int(tot_b),
+                 "kv_bytes_per_launch": int(kv_b), "flops_per_launch": fl})
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_per_layer_step, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "rows": p.rows, "heads": p.heads, "shards": p.num_shards,
+                   "topk": p.topk if sparse else None, "context": p.context,
+                   "kv": "fp8_e4m3 + fp32 per-token scale" if p.kv_dtype == "fp8" else "bf16",
+                   "page_size": p.page_size, "layers_per_step": lpt, "layers_rotated": n_layers,
+                   "step": ("remap once + fused decode for each layer sharing the table"
+                            if sparse else "fused dense decode")},
+        "kv_gbps": round(kv_gbps, 1),
+        "kv_pct_hbm_peak": round(100.0 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "decode_us_mean": round(dec_mean, 2),
+        "decode_us_p10_p90": [round(float(np.percentile(dec_us, 10)), 2),
+                              round(float(np.percentile(dec_us, 90)), 2)],
+        "remap_us_mean": round(statistics.mean(remap_us), 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline: copying one layer to the host", file=sys.stderr, flush=True)
+        w = groups[0]
+        host = (__import__("oracle").decode_bf16(w.q_host_bits()),
+                [w.pool_host(0, r) for r in range(p.num_shards)],
+                [w.scale_host(0, r) for r in range(p.num_shards)])
+        print("[bench] cpu baseline: running the oracle", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, host, args.cpu_rows)
+        result["cpu_baseline"] = cb
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -115,6 +115,11 @@ def _kv_dtype(pool):
 
 def remap_topk(topk_global, num_shards, shard=-1, out=None, counts=None, stream=None):
     """Global top-k slot table [rows, k] -> (local [S', rows, k], counts [S', rows])."""
+    return prepare_remap_topk(topk_global, num_shards, shard, out, counts, stream)()
+
+
+def prepare_remap_topk(topk_global, num_shards, shard=-1, out=None, counts=None, stream=None):
+    """As remap_topk, but returns a PreparedCall instead of calling."""
     _need(topk_global, torch.int32, "topk_global")
     rows, k = topk_global.shape
     n_out = num_shards if shard < 0 else 1
@@ -124,10 +129,10 @@ def remap_topk(topk_global, num_shards, shard=-1, out=None, counts=None, stream=
         counts = torch.empty((n_out, rows), dtype=torch.int32, device=topk_global.device)
     _need(out, torch.int32, "out", (n_out, rows, k))
     _need(counts, torch.int32, "counts", (n_out, rows))
-    _check(lib().dcp_remap_topk(_ptr(topk_global), rows, k, num_shards, shard, _ptr(out),
-                                _ptr(counts), _stream(topk_global.device, stream)),
-           "dcp_remap_topk")
-    return out, counts
+    args = (_ptr(topk_global), rows, k, num_shards, shard, _ptr(out), _ptr(counts),
+            _stream(topk_global.device, stream))
+    return PreparedCall(lib().dcp_remap_topk, args, "dcp_remap_topk", (out, counts),
+                        topk_global.device, (topk_global,))
 
 
 # ---------------------------------------------------------------- workspace
@@ -190,6 +195,22 @@ def _outputs(q, num_shards, want_partials, want_merged, out_dtype, out=None):
     return res
 
 
+class PreparedCall:
+    """A library call with every argument marshalled once (for launch loops).
+
+    Holds references to the tensors it points at.  Calling it queues the work
+    on the stream captured at preparation time (or the one given)."""
+
+    def __init__(self, fn, args, name, result, device, keep):
+        self._fn, self._args, self._name = fn, args, name
+        self.result, self._device, self._keep = result, device, keep
+
+    def __call__(self, stream=None):
+        args = self._args if stream is None else self._args[:-1] + (_stream(self._device, stream),)
+        _check(self._fn(*args), self._name)
+        return self.result
+
+
 def sparse_decode(q, pools, scales, topk_local, counts, softmax_scale, want_partials=False,
                   want_merged=True, out_dtype=OUT_F32, num_splits=0, workspace=None, out=None,
                   stream=None):
@@ -199,6 +220,15 @@ def sparse_decode(q, pools, scales, topk_local, counts, softmax_scale, want_part
     scales[r] fp32 [pool_rows] for FP8; topk_local int32 [N, rows, k];
     counts int32 [N, rows].  Returns a dict with o/lse and/or o_part/lse_part.
     """
+    return prepare_sparse_decode(q, pools, scales, topk_local, counts, softmax_scale,
+                                 want_partials, want_merged, out_dtype, num_splits, workspace,
+                                 out, stream)()
+
+
+def prepare_sparse_decode(q, pools, scales, topk_local, counts, softmax_scale,
+                          want_partials=False, want_merged=True, out_dtype=OUT_F32, num_splits=0,
+                          workspace=None, out=None, stream=None):
+    """As sparse_decode, but returns a PreparedCall instead of calling."""
     _need(q, torch.bfloat16, "q")
     rows, heads, _ = q.shape
     n = len(pools)
@@ -211,13 +241,13 @@ def sparse_decode(q, pools, scales, topk_local, counts, softmax_scale, want_part
     if workspace is None:
         nb = workspace_size(False, rows, heads, n, k, 1, num_splits, want_partials, want_merged)
         workspace = alloc_workspace(nb, q.device) if nb else None
-    st = lib().mla_sparse_decode_lse(
-        _ptr(q), rows, heads, shards, n, kv_dtype, _ptr(topk_local), _ptr(counts), k,
-        float(softmax_scale), _ptr(res.get("o_part")), _ptr(res.get("lse_part")),
-        _ptr(res.get("o")), _ptr(res.get("lse")), out_dtype, num_splits, _ptr(workspace),
-        0 if workspace is None else workspace.numel(), _stream(q.device, stream))
-    _check(st, "mla_sparse_decode_lse")
-    return res
+    args = (_ptr(q), rows, heads, shards, n, kv_dtype, _ptr(topk_local), _ptr(counts), k,
+            float(softmax_scale), _ptr(res.get("o_part")), _ptr(res.get("lse_part")),
+            _ptr(res.get("o")), _ptr(res.get("lse")), out_dtype, num_splits, _ptr(workspace),
+            0 if workspace is None else workspace.numel(), _stream(q.device, stream))
+    keep = (q, pools, scales, topk_local, counts, workspace)
+    return PreparedCall(lib().mla_sparse_decode_lse, args, "mla_sparse_decode_lse", res, q.device,
+                        keep)
 
 
 def dense_decode(q, pools, scales, block_table, local_lens, page_size, max_local_len,
@@ -227,6 +257,15 @@ def dense_decode(q, pools, scales, block_table, local_lens, page_size, max_local
 
     block_table int32 [rows, max_pages]; local_lens[r] int32 [rows].
     """
+    return prepare_dense_decode(q, pools, scales, block_table, local_lens, page_size,
+                                max_local_len, softmax_scale, want_partials, want_merged,
+                                out_dtype, num_splits, workspace, out, stream)()
+
+
+def prepare_dense_decode(q, pools, scales, block_table, local_lens, page_size, max_local_len,
+                         softmax_scale, want_partials=False, want_merged=True, out_dtype=OUT_F32,
+                         num_splits=0, workspace=None, out=None, stream=None):
+    """As dense_decode, but returns a PreparedCall instead of calling."""
     _need(q, torch.bfloat16, "q")
     rows, heads, _ = q.shape
     n = len(pools)
@@ -239,14 +278,14 @@ def dense_decode(q, pools, scales, block_table, local_lens, page_size, max_local
         nb = workspace_size(True, rows, heads, n, max_local_len, page_size, num_splits,
                             want_partials, want_merged)
         workspace = alloc_workspace(nb, q.device) if nb else None
-    st = lib().mla_dense_decode_lse(
-        _ptr(q), rows, heads, shards, n, kv_dtype, _ptr(block_table), block_table.shape[1],
-        page_size, max_local_len, float(softmax_scale), _ptr(res.get("o_part")),
-        _ptr(res.get("lse_part")), _ptr(res.get("o")), _ptr(res.get("lse")), out_dtype,
-        num_splits, _ptr(workspace), 0 if workspace is None else workspace.numel(),
-        _stream(q.device, stream))
-    _check(st, "mla_dense_decode_lse")
-    return res
+    args = (_ptr(q), rows, heads, shards, n, kv_dtype, _ptr(block_table), block_table.shape[1],
+            page_size, max_local_len, float(softmax_scale), _ptr(res.get("o_part")),
+            _ptr(res.get("lse_part")), _ptr(res.get("o")), _ptr(res.get("lse")), out_dtype,
+            num_splits, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+            _stream(q.device, stream))
+    keep = (q, pools, scales, block_table, local_lens, workspace)
+    return PreparedCall(lib().mla_dense_decode_lse, args, "mla_dense_decode_lse", res, q.device,
+                        keep)
 
 
 # ---------------------------------------------------------------- step 3

@@ -15,13 +15,17 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdcpmla.so")
-SOURCES = ["dcp_api.cpp", "dcp_remap.hip", "dcp_combine.hip", "dcp_decode.hip"]
+SOURCES = ["dcp_api.cpp", "dcp_remap.hip", "dcp_combine.hip", "dcp_decode.hip",
+           "dcp_decode_fp8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-lambda-capture",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in architectural VGPRs: the online-softmax rescale of
+    # O is then a plain VALU multiply instead of AGPR<->VGPR round trips
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 

@@ -36,6 +36,7 @@
 // shard is split] elects the last block, which merges the partials with LSE
 // weights and resets the counter for the next call.
 #include "dcp_device.h"
+#include "dcp_epilogue.h"
 #include "dcp_internal.h"
 
 namespace dcp {
@@ -68,54 +69,6 @@ constexpr int kStageBytes = kTileBytes + 256;            // + 64 fp32 scales (FP
 constexpr int kListOff = kStages * kStageBytes;
 constexpr int kSmemBytes = kListOff + kMaxList * 4;
 
-// Block-wide LSE merge of n_in partials [n_in][H][512] + [n_in][H] into one
-// [H][512] output (fp32 or bf16) + [H] LSE.  Weights in LDS.
-template <int NT>
-__device__ void merge_partials(const float* __restrict__ in_o, const float* __restrict__ in_lse,
-                               int n_in, int H, void* __restrict__ out_o, int out_bf16,
-                               float* __restrict__ out_lse, DCP_LDS float* wts) {
-  const int tid = threadIdx.x;
-  for (int h = tid; h < H; h += NT) {
-    float m = kNegInf;
-    for (int i = 0; i < n_in; ++i) {
-      float l = __builtin_nontemporal_load(in_lse + (size_t)i * H + h);
-      m = (l > m) ? l : m;
-    }
-    float wsum = 0.f;
-    for (int i = 0; i < n_in; ++i) {
-      float l = __builtin_nontemporal_load(in_lse + (size_t)i * H + h);
-      float w = (m > kNegInf && l > kNegInf) ? fast_exp2((l - m) * kLog2e) : 0.f;
-      wts[i * H + h] = w;
-      wsum += w;
-    }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    for (int i = 0; i < n_in; ++i) wts[i * H + h] *= inv;
-    out_lse[h] = wsum > 0.f ? m + logf(wsum) : kNegInf;
-  }
-  __syncthreads();
-  constexpr int C = kVDim / 4;
-  for (int idx = tid; idx < H * C; idx += NT) {
-    const int h = idx / C;
-    const int c = idx - h * C;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < n_in; ++i) {
-      const float w = wts[i * H + h];
-      if (w != 0.f) {
-        const f32x4 v = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(in_o + ((size_t)i * H + h) * kVDim) + c);
-        acc += w * v;
-      }
-    }
-    if (out_bf16) {
-      unsigned lo = f32_to_bf16_bits(acc[0]) | ((unsigned)f32_to_bf16_bits(acc[1]) << 16);
-      unsigned hi = f32_to_bf16_bits(acc[2]) | ((unsigned)f32_to_bf16_bits(acc[3]) << 16);
-      reinterpret_cast<uint2*>(out_o)[(size_t)h * C + c] = make_uint2(lo, hi);
-    } else {
-      reinterpret_cast<f32x4*>(out_o)[(size_t)h * C + c] = acc;
-    }
-  }
-}
-
 template <bool FP8, bool DENSE, int NW, int TS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const DecodeParams p) {
@@ -124,7 +77,6 @@ void decode_kernel(const DecodeParams p) {
   constexpr int NT = NW * 64;
   constexpr int HG = NW / TS;          // head groups of 16 in this block
   constexpr int TSUB = T / TS;         // tokens of a tile per token group
-  constexpr int NST = TSUB / 16;       // 16-token S tiles per wave per tile
   constexpr int NKB = TSUB / 32;       // 32-token PV blocks per wave per tile
   constexpr int IPW = (kTileBytes / 1024) / NW;   // DMA instructions per wave per tile
   static_assert(NKB >= 1 && IPW * NW * 1024 == kTileBytes, "tile split");
@@ -197,19 +149,71 @@ void decode_kernel(const DecodeParams p) {
     return min(max(r, 0LL), max_prow);
   };
 
-  // ---- query fragments (B operand of S^T = K Q^T), kept for the whole block
+  // ---- query fragments (B operand of S^T = K Q^T), kept for the whole block.
+  // BF16 KV: bf16 Q on the bf16 MFMA; k-step s covers dims 32s..32s+31 and
+  // lane group g holds dims 32s + 8g .. +8.
+  // FP8 KV: Q * 2^e is split into E4M3 hi + lo for the fp8 MFMA (K = 128):
+  // k-step s covers dims 128s..128s+127, lane group g holds dims 128s + 32g
+  // .. +32, dims >= 576 are zero.  e is per head, the largest power of two
+  // with max|q| * 2^e <= 448; hi + lo reproduces every bf16 element whose
+  // scaled magnitude is >= 2^-2 exactly, smaller ones to within 2^-10
+  // (scaled), i.e. to ~2^-16 of max|q|.
   const int head = hblk * kHeadsPerBlock + hg * 16 + i16;
   const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + head) * kHeadDim;
-  bf16x8 qf[18];
+  [[maybe_unused]] bf16x8 qf[FP8 ? 1 : 18];
+  [[maybe_unused]] i32x8 qhi[FP8 ? 5 : 1], qlo[FP8 ? 5 : 1];
+  float z_scale = p.sm_scale_log2;     // multiplies the raw MFMA logit
+  if constexpr (FP8) {
+    bf16x8 raw[5][4];
+    float qmax = 0.f;
 #pragma unroll
-  for (int s = 0; s < 18; ++s) {
-    const int dim = FP8 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
-    qf[s] = *reinterpret_cast<const bf16x8*>(qrow + dim);
+    for (int s = 0; s < 5; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int dim = 128 * s + 32 * g + 8 * u;
+        raw[s][u] = dim < kHeadDim ? *reinterpret_cast<const bf16x8*>(qrow + dim) : bf16x8{};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[s][u][j])));
+      }
+    qmax = wave_xor_max(qmax, 16);
+    qmax = wave_xor_max(qmax, 32);
+    int e = 0;
+    if (qmax > 0.f) {
+      int ex;
+      frexpf(448.0f / qmax, &ex);
+      e = min(max(ex - 1, -120), 120);
+      while (e > -120 && ldexpf(qmax, e) > 448.0f) --e;
+    }
+    const float qs = ldexpf(1.0f, e);
+    z_scale = p.sm_scale_log2 * ldexpf(1.0f, -e);
+#pragma unroll
+    for (int s = 0; s < 5; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float x[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = bf16_to_f32(raw[s][u][4 * half + j]) * qs;
+          int h = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+          h = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h, true);
+          const float r[4] = {x[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0),
+                              x[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1),
+                              x[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2),
+                              x[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3)};
+          int l = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+          l = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], l, true);
+          qhi[s][2 * u + half] = h;
+          qlo[s][2 * u + half] = l;
+        }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g);
+    // Complete the query loads here, so that no wait for them lands inside
+    // the tile loop (where it would also drain the in-flight KV copies).
+#pragma unroll
+    for (int s = 0; s < 18; ++s) touch(qf[s]);
   }
-  // Complete the query loads here, so that no wait for them lands inside the
-  // tile loop (where it would also drain the in-flight KV copies).
-#pragma unroll
-  for (int s = 0; s < 18; ++s) touch(qf[s]);
   __syncthreads();   // list visible
 
   auto issue_tile = [&](int it) {
@@ -235,7 +239,7 @@ void decode_kernel(const DecodeParams p) {
   };
 
   // ---- online-softmax state: per lane, head = hg*16 + i16; O^T tiles
-  float m_run = kNegInf;    // running max, base-2 logits
+  float m_run = kNegInf;    // reference max (base-2 logits), see the softmax below
   float l_run = 0.f;        // this lane's share of the running sum
   f32x4 oacc[32];
 #pragma unroll
@@ -256,132 +260,216 @@ void decode_kernel(const DecodeParams p) {
 
     const DCP_LDS char* sbase = smem + (it % kStages) * kStageBytes;
     const int tok0 = start + it * T;
-    const int sub0 = ts * TSUB;
 
-    // S^T = K Q^T for this wave's NST 16-token tiles
-    f32x4 sacc[NST];
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int t = sub0 + st * 16 + i16;
-      const DCP_LDS char* rp = sbase + t * RB;
-      const int sw = swz<FP8>(t);
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (FP8) {
-#pragma unroll
-        for (int s2 = 0; s2 < 9; ++s2) {
-          const i32x4 raw = *reinterpret_cast<const DCP_LDS i32x4*>(rp + 16 * ((4 * s2 + g) ^ sw));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(raw.x, raw.y), qf[2 * s2], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(raw.z, raw.w), qf[2 * s2 + 1], acc, 0, 0, 0);
-          if (s2 % 3 == 2) __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 18; ++s) {
-          const bf16x8 a = *reinterpret_cast<const DCP_LDS bf16x8*>(rp + 16 * ((4 * s + g) ^ sw));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], acc, 0, 0, 0);
-          if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      sacc[st] = acc;
-    }
-
-    // online softmax (lane: head column, tokens 4g..4g+3 of each S tile)
-    float z[NST][4];
-    float sc[NST][4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int tk = sub0 + st * 16 + 4 * g;
-      if constexpr (FP8) {
-        const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sbase + kTileBytes + 4 * tk);
-        sc[st][0] = s4[0]; sc[st][1] = s4[1]; sc[st][2] = s4[2]; sc[st][3] = s4[3];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = sacc[st][i] * p.sm_scale_log2;
-        if constexpr (FP8) v *= sc[st][i];
-        v = (tok0 + tk + i < end) ? v : kNegInf;
-        z[st][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    }
-    tmax = wave_xor_max(tmax, 16);
-    tmax = wave_xor_max(tmax, 32);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int d = 0; d < 32; ++d) oacc[d] *= alpha;
-    }
-    l_run *= alpha;
-    m_run = m_new;
-    float pr[NST][4];
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = fast_exp2(z[st][i] - m_use);
-        l_run += e;
-        pr[st][i] = FP8 ? e * sc[st][i] : e;
-      }
-    }
-
-    // O^T += V^T P^T, one 32-token block at a time.  k-slot j of lane group g
-    // is token 4g+j (j < 4) or 16+4g+(j-4) (j >= 4) of the block: exactly the
-    // tokens this lane holds in the two S tiles, so P needs no shuffle.
+    // The wave's share of the tile in 32-token chunks: S^T for two 16-token
+    // S tiles, the softmax update, then O^T += V^T P^T for those 32 tokens.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int blk0 = sub0 + 32 * kb;
+      const int sub0 = ts * TSUB + 32 * kb;
+      constexpr int CST = 2;   // S tiles per chunk
+
+      // S^T = K Q^T; the two S tiles are independent accumulators,
+      // interleaved so back-to-back MFMAs never wait on each other.  The
+      // operands of k-step s+1 are read from LDS while step s multiplies.
+      f32x4 sacc[CST];
+#pragma unroll
+      for (int st = 0; st < CST; ++st) sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (FP8) {
-        const f16x8 bp = f16x8{(_Float16)pr[2 * kb][0], (_Float16)pr[2 * kb][1],
-                               (_Float16)pr[2 * kb][2], (_Float16)pr[2 * kb][3],
-                               (_Float16)pr[2 * kb + 1][0], (_Float16)pr[2 * kb + 1][1],
-                               (_Float16)pr[2 * kb + 1][2], (_Float16)pr[2 * kb + 1][3]};
+        auto load_k = [&](int s, i32x8* a) {
+          const bool live = (s < 4) || (g < 2);     // dims 576..639 are padding
+          const int c0 = live ? 8 * s + 2 * g : 0;
+#pragma unroll
+          for (int st = 0; st < CST; ++st) {
+            const int t = sub0 + st * 16 + i16;
+            const DCP_LDS char* rp = sbase + t * RB;
+            const int sw = swz<FP8>(t);
+            const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp + 16 * (c0 ^ sw));
+            const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp + 16 * ((c0 + 1) ^ sw));
+            a[st] = live ? i32x8{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w} : i32x8{};
+          }
+        };
+        i32x8 a[2][CST];
+        load_k(0, a[0]);
+#pragma unroll
+        for (int s = 0; s < 5; ++s) {
+          if (s + 1 < 5) load_k(s + 1, a[(s + 1) & 1]);
+#pragma unroll
+          for (int st = 0; st < CST; ++st)
+            sacc[st] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s & 1][st], qhi[s], sacc[st],
+                                                                        0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int st = 0; st < CST; ++st)
+            sacc[st] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s & 1][st], qlo[s], sacc[st],
+                                                                        0, 0, 0, 127, 0, 127);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        auto load_k = [&](int s, bf16x8* a) {
+#pragma unroll
+          for (int st = 0; st < CST; ++st) {
+            const int t = sub0 + st * 16 + i16;
+            a[st] = *reinterpret_cast<const DCP_LDS bf16x8*>(
+                sbase + t * RB + 16 * ((4 * s + g) ^ swz<FP8>(t)));
+          }
+        };
+        bf16x8 a[3][CST];
+        load_k(0, a[0]);
+        load_k(1, a[1]);
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          if (s + 2 < 18) load_k(s + 2, a[(s + 2) % 3]);
+#pragma unroll
+          for (int st = 0; st < CST; ++st)
+            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s % 3][st], qf[s], sacc[st], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // First V^T operands of the chunk, read before the softmax so their
+      // LDS latency hides behind it (see the PV loop below for the layout).
+      const int blk0 = sub0;
+      [[maybe_unused]] i32x2 vraw[2][8];
+      [[maybe_unused]] i16x4 vr16[2][4][2];
+      [[maybe_unused]] const DCP_LDS char* vp = nullptr;
+      [[maybe_unused]] int vsw = 0;
+      [[maybe_unused]] const DCP_LDS char* va = nullptr;
+      [[maybe_unused]] const DCP_LDS char* vb = nullptr;
+      [[maybe_unused]] int swa = 0, swb = 0, vhalf = 0;
+      if constexpr (FP8) {
         // tr8: lane i of a 16-lane group receives byte i%8 from the lanes
         // (i/8) + 2j; lane L therefore points at token slot L/2, bytes
         // [16d + 8(L%2), +8) -- lane i ends up with dim 16d + i of 8 tokens.
         const int jj = i16 >> 1;
         const int tk = blk0 + (jj < 4 ? 4 * g + jj : 16 + 4 * g + (jj - 4));
-        const DCP_LDS char* vp = sbase + tk * RB + 8 * (i16 & 1);
-        const int sw = swz<FP8>(tk);
+        vp = sbase + tk * RB + 8 * (i16 & 1);
+        vsw = swz<FP8>(tk);
 #pragma unroll
-        for (int d = 0; d < 32; ++d) {
-          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (DCP_LDS i32x2*)(vp + 16 * (d ^ sw)));
-          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(raw.x, raw.y), bp, oacc[d], 0, 0, 0);
-          if (d % 8 == 7) __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int j = 0; j < 8; ++j)
+          vraw[0][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DCP_LDS i32x2*)(vp + 16 * (j ^ vsw)));
       } else {
-        bf16x8 bh, bl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = pr[2 * kb + (j >> 2)][j & 3];
-          const __bf16 hi = f32_to_bf16(v);
-          bh[j] = hi;
-          bl[j] = f32_to_bf16(v - bf16_to_f32(hi));
-        }
         // tr16: lane i receives element i%4 from the lanes (i/4) + 4j; lane L
         // points at token slot L/4 (+4 for the second read), elements
         // [16d + 4(L%4), +4) -- lane i ends up with dim 16d + i of 4 tokens.
         const int tka = blk0 + 4 * g + (i16 >> 2);
         const int tkb = blk0 + 16 + 4 * g + (i16 >> 2);
-        const int swa = swz<FP8>(tka), swb = swz<FP8>(tkb);
-        const int half = (i16 & 3) >> 1;
-        const DCP_LDS char* va = sbase + tka * RB + 8 * (i16 & 1);
-        const DCP_LDS char* vb = sbase + tkb * RB + 8 * (i16 & 1);
+        swa = swz<FP8>(tka);
+        swb = swz<FP8>(tkb);
+        vhalf = (i16 & 3) >> 1;
+        va = sbase + tka * RB + 8 * (i16 & 1);
+        vb = sbase + tkb * RB + 8 * (i16 & 1);
 #pragma unroll
-        for (int d = 0; d < 32; ++d) {
-          const i16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DCP_LDS i16x4*)(va + 16 * ((2 * d + half) ^ swa)));
-          const i16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DCP_LDS i16x4*)(vb + 16 * ((2 * d + half) ^ swb)));
-          const i32x2 ra2 = __builtin_bit_cast(i32x2, ra);
-          const i32x2 rb2 = __builtin_bit_cast(i32x2, rb);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, i32x4{ra2.x, ra2.y, rb2.x, rb2.y});
-          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[d], 0, 0, 0);
-          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, oacc[d], 0, 0, 0);
-          if (d % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) {
+          vr16[0][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (DCP_LDS i16x4*)(va + 16 * ((2 * j + vhalf) ^ swa)));
+          vr16[0][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (DCP_LDS i16x4*)(vb + 16 * ((2 * j + vhalf) ^ swb)));
+        }
+      }
+
+      // Online softmax (lane: head column, tokens 4g..4g+3 of each S tile).
+      // The reference max m_run only moves when the chunk max exceeds it by
+      // more than 8 (base 2): p = 2^(z - m_run) then stays <= 2^8, and O and
+      // l are rescaled rarely instead of on every chunk.
+      float z[CST][4];
+      float sc[CST][4];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int st = 0; st < CST; ++st) {
+        const int tk = sub0 + st * 16 + 4 * g;
+        if constexpr (FP8) {
+          const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sbase + kTileBytes + 4 * tk);
+          sc[st][0] = s4[0]; sc[st][1] = s4[1]; sc[st][2] = s4[2]; sc[st][3] = s4[3];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sacc[st][i] * z_scale;
+          if constexpr (FP8) v *= sc[st][i];
+          v = (tok0 + tk + i < end) ? v : kNegInf;
+          z[st][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      }
+      tmax = wave_xor_max(tmax, 16);
+      tmax = wave_xor_max(tmax, 32);
+      const bool bump = tmax > m_run + 8.0f;
+      if (__any(bump)) {
+        const float m_new = bump ? tmax : m_run;
+        const float alpha = bump ? fast_exp2(m_run - m_new) : 1.0f;   // m_run = -inf -> 0
+        if (__any(bump && m_run != kNegInf)) {
+#pragma unroll
+          for (int d = 0; d < 32; ++d) oacc[d] *= alpha;
+        }
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+      float pr[CST][4];
+#pragma unroll
+      for (int st = 0; st < CST; ++st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(z[st][i] - m_use);
+          l_run += e;
+          pr[st][i] = FP8 ? e * sc[st][i] : e;
+        }
+      }
+
+      // O^T += V^T P^T over the chunk's 32 tokens.  k-slot j of lane group g
+      // is token 4g+j (j < 4) or 16+4g+(j-4) (j >= 4) of the chunk: exactly
+      // the tokens this lane holds in the two S tiles, so P needs no shuffle.
+      // V^T operands are read in groups of 8 (FP8) / 4 (BF16) 16-dim tiles,
+      // one group ahead of the MFMAs that consume them.
+      if constexpr (FP8) {
+        const f16x8 bp = f16x8{(_Float16)pr[0][0], (_Float16)pr[0][1], (_Float16)pr[0][2],
+                               (_Float16)pr[0][3], (_Float16)pr[1][0], (_Float16)pr[1][1],
+                               (_Float16)pr[1][2], (_Float16)pr[1][3]};
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          if (grp + 1 < 4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              vraw[(grp + 1) & 1][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                  (DCP_LDS i32x2*)(vp + 16 * ((8 * (grp + 1) + j) ^ vsw)));
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const i32x2 raw = vraw[grp & 1][j];
+            oacc[8 * grp + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(raw.x, raw.y), bp,
+                                                                       oacc[8 * grp + j], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        bf16x8 bh, bl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = pr[j >> 2][j & 3];
+          const __bf16 hi = f32_to_bf16(v);
+          bh[j] = hi;
+          bl[j] = f32_to_bf16(v - bf16_to_f32(hi));
+        }
+#pragma unroll
+        for (int grp = 0; grp < 8; ++grp) {
+          if (grp + 1 < 8) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int d = 4 * (grp + 1) + j;
+              vr16[(grp + 1) & 1][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (DCP_LDS i16x4*)(va + 16 * ((2 * d + vhalf) ^ swa)));
+              vr16[(grp + 1) & 1][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (DCP_LDS i16x4*)(vb + 16 * ((2 * d + vhalf) ^ swb)));
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d = 4 * grp + j;
+            const i32x2 ra2 = __builtin_bit_cast(i32x2, vr16[grp & 1][j][0]);
+            const i32x2 rb2 = __builtin_bit_cast(i32x2, vr16[grp & 1][j][1]);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, i32x4{ra2.x, ra2.y, rb2.x, rb2.y});
+            oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[d], 0, 0, 0);
+            oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, oacc[d], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -422,68 +510,7 @@ void decode_kernel(const DecodeParams p) {
     }
   }
 
-  const bool need_shard_merge = p.o_part != nullptr && S > 1;
-  const bool fused = p.o != nullptr;
-  const bool to_ws = fused || need_shard_merge;
-  const bool to_part = p.o_part != nullptr && S == 1;
-  if (ts == 0) {
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
-    const long long blk_part = ((row * N + shard) * S + split);
-    float* wo = to_ws ? p.ws_o + (blk_part * H + head) * kVDim : nullptr;
-    float* po = to_part ? p.o_part + (((long long)shard * p.rows + row) * H + head) * kVDim : nullptr;
-#pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const float4 v = make_float4(oacc[d][0] * inv, oacc[d][1] * inv, oacc[d][2] * inv, oacc[d][3] * inv);
-      const int dim = 16 * d + 4 * g;
-      if (to_ws) *reinterpret_cast<float4*>(wo + dim) = v;
-      if (to_part) *reinterpret_cast<float4*>(po + dim) = v;
-    }
-    if (g == 0) {
-      if (to_ws) p.ws_lse[blk_part * H + head] = lse_v;
-      if (to_part) p.lse_part[((long long)shard * p.rows + row) * H + head] = lse_v;
-    }
-  }
-  if (!to_ws) return;
-
-  // ---- elect the last block and merge (release: fence then count;
-  // acquire: fence after winning)
-  __syncthreads();
-  DCP_LDS float* wts = (DCP_LDS float*)smem;
-  if (need_shard_merge) {
-    if (tid == 0) {
-      __threadfence();
-      const int old = atomicAdd(p.cnt_shard + row * N + shard, 1);
-      s_flag = (old == S * HB - 1);
-    }
-    __syncthreads();
-    if (s_flag) {
-      __threadfence();
-      const long long base = (row * N + shard) * S;
-      merge_partials<NT>(p.ws_o + base * H * kVDim, p.ws_lse + base * H, S, H,
-                         p.o_part + ((long long)shard * p.rows + row) * H * kVDim, 0,
-                         p.lse_part + ((long long)shard * p.rows + row) * H, wts);
-      if (tid == 0) p.cnt_shard[row * N + shard] = 0;
-    }
-    __syncthreads();
-  }
-  if (fused) {
-    if (tid == 0) {
-      __threadfence();
-      const int old = atomicAdd(p.cnt_row + row, 1);
-      s_flag = (old == N * S * HB - 1);
-    }
-    __syncthreads();
-    if (s_flag) {
-      __threadfence();
-      const long long base = row * N * S;
-      void* out = p.out_bf16 ? (void*)(static_cast<unsigned short*>(p.o) + row * H * kVDim)
-                             : (void*)(static_cast<float*>(p.o) + row * H * kVDim);
-      merge_partials<NT>(p.ws_o + base * H * kVDim, p.ws_lse + base * H, N * S, H, out,
-                         p.out_bf16, p.lse + row * H, wts);
-      if (tid == 0) p.cnt_row[row] = 0;
-    }
-  }
+  finish_block<NT>(p, row, shard, split, head, g, ts == 0, oacc, m_run, l_tot, smem, &s_flag);
 }
 
 template <bool FP8, bool DENSE, int NW, int TS>
@@ -515,6 +542,7 @@ hipError_t launch_heads(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream) {
+  if (fp8 && (p.heads == 64 || p.heads == 128)) return launch_decode_fp8(p, dense, stream);
   if (fp8) return dense ? launch_heads<true, true>(p, stream) : launch_heads<true, false>(p, stream);
   return dense ? launch_heads<false, true>(p, stream) : launch_heads<false, false>(p, stream);
 }

@@ -1,0 +1,403 @@
+// Step 2 (+ step 3 fused) for FP8 E4M3 KV with 64 or 128 gathered heads:
+// absorbed-weight MLA decode with LSE over one DCP shard's paged latent KV,
+// the shards' partials merged in the epilogue of the last block of a row.
+//
+// Pages: [P3] "[DSA] Fix decode context parallelism for RoPE sparse attention
+// on Blackwell" -- Motivation (output and LSE from the backend; every rank
+// runs the heads of the whole DCP group), Modifications (Backend: return_lse,
+// rows without local KV fixed up, partials merged), Follow-ups item 1 (pack
+// and combine fused).  [P1] "feat: support decode context parallelism for
+// PyTorch MLA", Summary (dense and sparse FlashMLA with FP8 KV).
+//
+// Both contractions run on the gfx950 fp8 MFMA (16x16x128, f8f6f4 with E8M0
+// block scales), so no KV element is ever converted in registers:
+//   * S^T = K Q^T: K codes straight from LDS; Q*2^e split into E4M3 hi + lo
+//     once per block (exact for all but the tiniest elements).
+//   * O^T += V^T P'^T with P' = p * scale_t: P' of each lane's 32 tokens is
+//     scaled by a power of two to the top of the E4M3 range and split into
+//     three E4M3 terms (12 significant bits, like fp16), and the MFMA's B
+//     block scale (2^-e) undoes the power of two exactly.
+//
+// Data movement.  A tile is 128 tokens.  Its 576-byte rows are copied from
+// HBM straight into LDS with global->LDS DMA in a chunk-major layout,
+// [36 chunks of 16 bytes][128 token slots], one token per lane, so every
+// lane computes one row address per tile and the 18 copies it issues step
+// through that row 16 bytes at a time.  Two stages: tile it+1 streams in while tile it
+// is computed.  The slot ids (sparse) or page ids (dense) of tile it+2 are
+// DMA'd into a three-deep ring at the same time, so the row addresses of the
+// next tile are ready without a dependent global load.
+//
+// Per wave: 16 heads (4 waves = 64 heads; 128 heads use two blocks).  Per
+// tile: 8 S tiles x 5 k-steps x 2 (hi, lo) + 32 dim tiles x 3 (P' terms) =
+// 176 MFMAs of 16x16x128.
+#include "dcp_device.h"
+#include "dcp_epilogue.h"
+#include "dcp_internal.h"
+
+namespace dcp {
+namespace {
+
+constexpr int kT = 128;                            // tokens per tile
+constexpr int kRowBytes = 576;                     // E4M3 codes per key row
+constexpr int kChunks = 36;                        // 16-byte chunks per row
+constexpr int kPlane = kT * 16;                    // LDS bytes of one chunk plane
+constexpr int kTileBytes = kChunks * kPlane;       // 73728
+constexpr int kStageBytes = kTileBytes + kT * 4;   // + per-token scales
+constexpr int kRingOff = 2 * kStageBytes;          // slot/page-id ring, 3 tiles
+constexpr int kSmem = kRingOff + 3 * kT * 4;       // 150016 bytes
+constexpr int kThreads = 256;
+
+// LDS slot of token t inside a chunk plane (an involution).  Tokens 16..31 of
+// every 32 swap 8-slot halves, so that the two 4-token groups one 16-lane
+// group gathers with a transposing read fall in different bank halves.
+__device__ __forceinline__ int slot_of(int t) { return t ^ (((t >> 4) & 1) << 3); }
+
+// Four E4M3 codes (RNE) of four floats, in byte order.
+__device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, h, true);
+}
+
+// Largest e with x * 2^e <= 448 (the E4M3 maximum); 0 for x == 0.
+__device__ __forceinline__ int e4m3_exponent(float x) {
+  if (!(x > 0.f)) return 0;
+  int ex;
+  frexpf(448.0f / x, &ex);
+  int e = min(max(ex - 1, -120), 120);
+  while (e > -120 && ldexpf(x, e) > 448.0f) --e;
+  return e;
+}
+
+template <bool DENSE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_fp8_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
+  __shared__ int s_flag;
+  DCP_LDS char* smem = (DCP_LDS char*)smem_raw;
+  DCP_LDS int* ring = (DCP_LDS int*)(smem + kRingOff);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;             // 16-lane group of the MFMA layouts
+  const int i16 = lane & 15;
+
+  // ---- block -> (row, shard, split, head block); a row's blocks are
+  // consecutive within one XCD's share of the grid
+  long long b = blockIdx.x;
+  if (p.xcd_swizzle) {
+    const long long per_xcd = (long long)gridDim.x >> 3;
+    b = (b & 7) * per_xcd + (b >> 3);
+  }
+  const int HB = p.head_blocks, S = p.num_splits, N = p.num_shards;
+  const int hblk = (int)(b % HB); b /= HB;
+  const int split = (int)(b % S); b /= S;
+  const int shard = (int)(b % N);
+  const long long row = b / N;
+  const int H = p.heads;
+
+  const ShardArg sh = p.shard[shard];
+  const char* kvbase = static_cast<const char*>(sh.kv);
+  const int max_prow = (int)min(sh.pool_rows - 1, (long long)0x7fffffff);
+
+  // ---- this block's token range [start, end) of the shard's local tokens
+  int n_tok;
+  if constexpr (DENSE) {
+    n_tok = (int)min((long long)sh.local_len[row], (long long)p.max_pages * p.page_size);
+  } else {
+    n_tok = min(p.counts[(long long)shard * p.rows + row], p.k);
+  }
+  n_tok = max(n_tok, 0);
+  const int chunk = ((n_tok + S - 1) / S + kT - 1) / kT * kT;
+  const int start = min(n_tok, split * chunk);
+  const int end = min(n_tok, start + chunk);
+  const int ntiles = (end - start + kT - 1) / kT;
+
+  // Where the id of local token j lives: the compacted slot id (sparse) or
+  // the page id of its logical page (dense).
+  const int page = DENSE ? p.page_size : 1;
+  const int* ids = DENSE ? p.block_table + row * p.max_pages
+                         : p.topk_local + ((long long)shard * p.rows + row) * p.k;
+  auto id_ptr = [&](int j) -> const int* { return DENSE ? ids + j / page : ids + j; };
+  auto pool_row = [&](int j, int id) -> int {
+    const int r = DENSE ? id * page + (j - (j / page) * page) : id;
+    return min(max(r, 0), max_prow);
+  };
+
+  // ---- ids of tiles 0 and 1 with plain loads (nothing else is in flight)
+  for (int i = tid; i < 2 * kT; i += kThreads) {
+    const int it = i / kT, t = i - it * kT;
+    if (it < ntiles) {
+      const int tok0 = start + it * kT;
+      const int nval = min(kT, end - tok0);
+      ring[it * kT + t] = *id_ptr(tok0 + (t < nval ? t : 0));
+    }
+  }
+
+  // ---- query: Q * 2^e as E4M3 hi + lo, k-step s covers dims 128s..128s+127
+  // and lane group g holds dims 128s + 32g .. +32 (dims >= 576 are zero).
+  const int head = hblk * kHeadsPerBlock + wave * 16 + i16;
+  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + head) * kHeadDim;
+  i32x8 qhi[5], qlo[5];
+  float z_scale;
+  {
+    bf16x8 raw[5][4];
+    float qmax = 0.f;
+#pragma unroll
+    for (int s = 0; s < 5; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int dim = 128 * s + 32 * g + 8 * u;
+        raw[s][u] = dim < kHeadDim ? *reinterpret_cast<const bf16x8*>(qrow + dim) : bf16x8{};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[s][u][j])));
+      }
+    qmax = wave_xor_max(qmax, 16);
+    qmax = wave_xor_max(qmax, 32);
+    const int e = e4m3_exponent(qmax);
+    const float qs = ldexpf(1.0f, e);
+    z_scale = p.sm_scale_log2 * ldexpf(1.0f, -e);
+#pragma unroll
+    for (int s = 0; s < 5; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float x[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = bf16_to_f32(raw[s][u][4 * half + j]) * qs;
+          const int h = pack_e4m3(x[0], x[1], x[2], x[3]);
+          const int l = pack_e4m3(x[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0),
+                                  x[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1),
+                                  x[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2),
+                                  x[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3));
+          qhi[s][2 * u + half] = h;
+          qlo[s][2 * u + half] = l;
+        }
+  }
+  __syncthreads();   // ring slots 0 and 1 visible
+
+  // ---- copies.  Rows (and scales) of tile `it` into stage it & 1: wave w
+  // fills token slots 64*(w & 1) .. +63, one per lane, for chunk planes
+  // 18*(w >> 1) .. +17; waves 0 and 1 also copy the slots' scales.
+  auto issue_rows = [&](int it) {
+    DCP_LDS char* sb = smem + (it & 1) * kStageBytes;
+    const int h = wave & 1;
+    const int t = slot_of(64 * h + lane);          // token held in this lane's slot
+    const int tok0 = start + it * kT;
+    const int nval = min(kT, end - tok0);
+    const int tt = t < nval ? t : 0;               // padding re-reads token 0
+    const int prow = pool_row(tok0 + tt, ring[(it % 3) * kT + tt]);
+    const int c0 = 18 * (wave >> 1);
+    const char* src = kvbase + (long long)prow * kRowBytes + 16 * c0;
+    DCP_LDS char* dst = sb + c0 * kPlane + 1024 * h;
+#pragma unroll
+    for (int cc = 0; cc < 18; ++cc) dma16(src + 16 * cc, dst + cc * kPlane);
+    if (wave < 2) dma4(sh.scale + prow, sb + kTileBytes + 256 * h);
+  };
+  // Ids of tile `it` into ring slot it % 3 (waves 2 and 3, 64 tokens each).
+  auto issue_ring = [&](int it) {
+    const int t = (wave - 2) * 64 + lane;
+    const int tok0 = start + it * kT;
+    const int nval = min(kT, end - tok0);
+    dma4(id_ptr(tok0 + (t < nval ? t : 0)), ring + (it % 3) * kT + (wave - 2) * 64);
+  };
+
+  // ---- online-softmax state; lane: head column, O^T dims 16d + 4g + i
+  float m_run = kNegInf;    // reference max (base-2 logits), moves lazily
+  float l_run = 0.f;        // this lane's share of sum 2^(z - m_run)
+  f32x4 oacc[32];
+#pragma unroll
+  for (int d = 0; d < 32; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // per-lane LDS offsets (bytes) inside a stage
+  // QK: token 16st + i16 of S tile st sits in slot 16st + (i16 ^ 8(st & 1));
+  // lane group g reads chunks 8s + 2g and 8s + 2g + 1 (s = 4: g < 2 only).
+  const int qk_even = 2 * g * kPlane + 16 * i16;
+  const int qk_odd = 2 * g * kPlane + 16 * (i16 ^ 8);
+  const int qk4_even = 2 * (g & 1) * kPlane + 16 * i16;
+  const int qk4_odd = 2 * (g & 1) * kPlane + 16 * (i16 ^ 8);
+  // PV: tr8 read r of lane L (group g) fetches token 32r + 16(jj >= 4) + 4g +
+  // (jj & 3), jj = L/2, bytes 8(L & 1) of a 16-byte chunk: lane i of the
+  // group then holds dim 16d + i of the 8 tokens of k-slots 8r..8r+7.
+  const int jj = i16 >> 1;
+  const int pv_slot = (jj < 4) ? (4 * g + (jj & 3)) : (16 + ((4 * g + (jj & 3)) ^ 8));
+  const int pv_off = 16 * pv_slot + 8 * (i16 & 1);
+  // softmax: the scales of tokens 16st + 4g .. +3 sit in slots 16st + (4g ^ 8(st & 1)) ..
+  const int sc_even = 4 * (4 * g);
+  const int sc_odd = 4 * ((4 * g) ^ 8);
+
+  if (ntiles > 0) issue_rows(0);
+
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vmcnt<0>();
+    lds_barrier();                       // tile it, its scales and ring(it + 1) landed
+    if (wave >= 2 && it + 2 < ntiles) issue_ring(it + 2);
+    if (it + 1 < ntiles) issue_rows(it + 1);
+
+    const DCP_LDS char* sb = smem + (it & 1) * kStageBytes;
+    const int tok0 = start + it * kT;
+
+    // ---- S^T = K Q^T, eight 16-token S tiles in two passes of four
+    f32x4 sacc[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto load_k = [&](int s, i32x8* a) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int st = 4 * half + q;
+          const int base = (s < 4) ? ((st & 1) ? qk_odd : qk_even) + 8 * s * kPlane
+                                   : ((st & 1) ? qk4_odd : qk4_even) + 32 * kPlane;
+          const DCP_LDS char* rp = sb + base + 256 * st;
+          const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp);
+          const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp + kPlane);
+          const bool live = (s < 4) || (g < 2);      // dims 576..639 are padding
+          a[q] = live ? i32x8{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w} : i32x8{};
+        }
+      };
+      i32x8 a[2][4];
+      load_k(0, a[0]);
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        if (s + 1 < 5) load_k(s + 1, a[(s + 1) & 1]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s & 1][q], qhi[s], acc[q], 0, 0,
+                                                                   0, 127, 0, 127);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s & 1][q], qlo[s], acc[q], 0, 0,
+                                                                   0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sacc[4 * half + q] = acc[q];
+    }
+
+    // First V^T operands, read before the softmax so their latency hides.
+    i32x2 vr[2][4][4];
+    auto load_v = [&](int d, i32x2* r4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (DCP_LDS i32x2*)(sb + d * kPlane + 512 * r + pv_off));
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_v(j, vr[0][j]);
+
+    // ---- online softmax over the tile (lane: tokens 16st + 4g + i).  The
+    // reference max only moves when the tile max exceeds it by more than 8
+    // (base 2), so O and l are rescaled rarely; p stays <= 2^8.
+    float z[8][4], sc[8][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(
+          sb + kTileBytes + 64 * st + ((st & 1) ? sc_odd : sc_even));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[st][i] = s4[i];
+        float v = sacc[st][i] * z_scale * s4[i];
+        v = (tok0 + 16 * st + 4 * g + i < end) ? v : kNegInf;
+        z[st][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = wave_xor_max(tmax, 16);
+    tmax = wave_xor_max(tmax, 32);
+    const bool bump = tmax > m_run + 8.0f;
+    if (__any(bump)) {
+      const float m_new = bump ? tmax : m_run;
+      const float alpha = bump ? fast_exp2(m_run - m_new) : 1.0f;   // m_run = -inf -> 0
+      if (__any(bump && m_run != kNegInf)) {
+#pragma unroll
+        for (int d = 0; d < 32; ++d) oacc[d] *= alpha;
+      }
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    float pr[8][4];
+    float pmax = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = fast_exp2(z[st][i] - m_use);
+        l_run += e;
+        pr[st][i] = e * sc[st][i];
+        pmax = fmaxf(pmax, pr[st][i]);
+      }
+
+    // ---- P' of the head's 128 tokens as three E4M3 terms at one power of two
+    // per head; the MFMA's B block scale (127 - ep) multiplies it back out.
+    // The power must be the same in the head's four lanes: in the 16x16x128
+    // operand layout lane group g holds k = 16g..16g+15 (bytes 0..15) and
+    // 64+16g..64+16g+15 (bytes 16..31), while the scale of the 32-wide k block
+    // kb is taken from lane group kb, so every scale block spans two groups.
+    pmax = wave_xor_max(pmax, 16);
+    pmax = wave_xor_max(pmax, 32);
+    const int ep = e4m3_exponent(pmax);
+    const float ps = ldexpf(1.0f, ep);
+    const int pscale = 127 - ep;
+    i32x8 p3[3];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = pr[st][i] * ps;
+      const int h = pack_e4m3(x[0], x[1], x[2], x[3]);
+      float r[4];
+      r[0] = x[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0);
+      r[1] = x[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1);
+      r[2] = x[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2);
+      r[3] = x[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3);
+      const int m = pack_e4m3(r[0], r[1], r[2], r[3]);
+      const int l = pack_e4m3(r[0] - __builtin_amdgcn_cvt_f32_fp8(m, 0),
+                              r[1] - __builtin_amdgcn_cvt_f32_fp8(m, 1),
+                              r[2] - __builtin_amdgcn_cvt_f32_fp8(m, 2),
+                              r[3] - __builtin_amdgcn_cvt_f32_fp8(m, 3));
+      p3[0][st] = h;
+      p3[1][st] = m;
+      p3[2][st] = l;
+    }
+
+    // ---- O^T += V^T P'^T: 32 dim tiles, operands one group of 4 ahead
+#pragma unroll
+    for (int grp = 0; grp < 8; ++grp) {
+      if (grp + 1 < 8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) load_v(4 * (grp + 1) + j, vr[(grp + 1) & 1][j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const i32x2* r4 = vr[grp & 1][j];
+        const i32x8 vt = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
+        const int d = 4 * grp + j;
+#pragma unroll
+        for (int term = 0; term < 3; ++term)
+          oacc[d] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vt, p3[term], oacc[d], 0, 0, 0,
+                                                                    127, 0, pscale);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  finish_block<kThreads>(p, row, shard, split, head, g, true, oacc, m_run, l_tot, smem, &s_flag);
+}
+
+}  // namespace
+
+hipError_t launch_decode_fp8(const DecodeParams& p, bool dense, hipStream_t stream) {
+  const long long blocks = p.rows * p.num_shards * (long long)p.num_splits * p.head_blocks;
+  void* args[] = {(void*)&p};
+  const void* fn = dense ? (const void*)decode_fp8_kernel<true> : (const void*)decode_fp8_kernel<false>;
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace dcp

@@ -14,6 +14,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 #define DCP_LDS __attribute__((address_space(3)))
@@ -47,6 +48,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Direct global -> LDS copies: lane l's bytes land at lds_base + l * size.
 // lds_base must be the same for the whole wave (it is read from lane 0).
+// (The instruction's immediate offset field would be added to the LDS
+// address as well as to the global one, so these helpers never use it.)
 __device__ __forceinline__ void dma16(const void* src, DCP_LDS void* lds_base) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");

@@ -77,5 +77,6 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int num_sh
                           long long rows, int heads, int dv, void* o, float* lse,
                           int out_bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeParams& p, bool dense, hipStream_t stream);
 
 }  // namespace dcp
