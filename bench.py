@@ -15,6 +15,8 @@ on the launch stream) and the CPU fp64 oracle timed on the host as a baseline.
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -29,6 +31,48 @@ from sharded_kv_sparse_amd import workloads as wl
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_digest():
+    """sha256 over the kernel sources (sorted by path): a traffic figure
+    measured on other sources is stale."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "sharded_kv_sparse_amd", "csrc", "*")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what
+    the counter reads for a copy of known size), or None when there is no
+    summary or it was taken on different sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def decode_kernel_name(p):
+    if p.kv_dtype == "fp8" and p.heads in (64, 128):
+        return "decode_fp8_kernel"
+    return "decode_kernel"
 METRIC = "µs/layer-step and KV HBM GB/s (% of peak), sparse MLA decode B=64 top-k 2048"
 
 
@@ -45,6 +89,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the CPU-baseline sample (0 = all rows of one layer-step)")
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
+    ap.add_argument("--print-digest", action="store_true",
+                    help="print the digest of the kernel sources that traffic figures are keyed on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -79,8 +125,9 @@ def flops(p, tokens):
     return 2.0 * p.heads * tokens * (576 + 512)
 
 
-def cpu_baseline(w, host, rows):
-    """Time the CPU oracle on one layer-step (or a row sample of it)."""
+def cpu_baseline(w, host, rows, min_seconds=10.0, max_reps=30):
+    """Time the CPU oracle on one layer-step (or a row sample of it),
+    repeated until about min_seconds of CPU work have run."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -91,7 +138,8 @@ def cpu_baseline(w, host, rows):
     q, pools, scales = host
     sel = np.arange(p.rows) if rows <= 0 else np.arange(min(rows, p.rows))
     times = []
-    for _ in range(3):
+    t_all = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_all < min_seconds and len(times) < max_reps):
         t0 = time.perf_counter()
         if p.kind == "sparse":
             local, counts = oracle.remap_topk(w.table[sel], p.num_shards, p.pool_rows)
@@ -109,7 +157,8 @@ def cpu_baseline(w, host, rows):
             "kind": "oracle",
             "sample": (f"{'all' if len(sel) == p.rows else len(sel)} of {p.rows} rows of one "
                        f"layer-step (remap + {p.num_shards} shard attentions + merge, fp64 numpy), "
-                       f"median of 3, scaled to {p.rows} rows; host {platform.processor() or 'cpu'}")}
+                       f"median of {len(times)} runs ({time.perf_counter() - t_all:.1f} s of CPU work), "
+                       f"scaled to {p.rows} rows; host {platform.processor() or 'cpu'}")}
 
 
 def main():
@@ -118,6 +167,9 @@ def main():
         print("bench.py runs on one GPU only: the DCP shards are cache slices on one device and "
               "this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.print_digest:
+        print(source_digest())
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -214,19 +266,25 @@ def main():
     dec_mean = statistics.mean(dec_us)
     fl = flops(p, tok)
     kv_gbps = kv_b / (us_per_layer_step * 1e-6) / 1e9
-    mfma_bound = (fl / (BF16_MFMA_PEAK_TFLOPS * 1e12)) > (tot_b / (HBM_PEAK_GBPS * 1e9))
+    # The FP8 path contracts on the fp8 MFMA, the BF16 path on the bf16 one.
+    mfma_peak = FP8_MFMA_PEAK_TFLOPS if p.kv_dtype == "fp8" else BF16_MFMA_PEAK_TFLOPS
+    mfma_bound = (fl / (mfma_peak * 1e12)) > (tot_b / (HBM_PEAK_GBPS * 1e9))
+    kname = decode_kernel_name(p)
+    traffic = measured_traffic(kname, p.name)
     if mfma_bound:
         achieved = fl / (dec_mean * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4), "traffic": traffic}
     else:
         achieved = tot_b / (dec_mean * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
-    roof.update({"kernel": "decode_kernel (fused sparse MLA decode + LSE merge)" if sparse
-                 else "decode_kernel (fused dense MLA decode + LSE merge)",
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    roof.update({"kernel": kname + (" (fused sparse MLA decode + LSE merge)" if sparse
+                                    else " (fused dense MLA decode + LSE merge)"),
                  "avg_launch_us": round(dec_mean, 2), "algorithmic_bytes_per_launch": int(tot_b),
-                 "kv_bytes_per_launch": int(kv_b), "flops_per_launch": fl})
+                 "kv_bytes_per_launch": int(kv_b), "flops_per_launch": fl,
+                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                 "copy-calibrated)"})
 
     result = {
         "metric": METRIC,
@@ -239,7 +297,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if p.kv_dtype == "fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": p.name, "rows": p.rows, "heads": p.heads, "shards": p.num_shards,
                    "topk": p.topk if sparse else None, "context": p.context,

@@ -117,9 +117,16 @@ dcp_status dcp_remap_topk(const int32_t* topk_global, int64_t rows, int32_t k,
  * (0 = library default); want_partials / want_merged = whether
  * (o_part, lse_part) / (o, lse) will be given.  Returns 0 when the call needs
  * no workspace, and SIZE_MAX for arguments the decode call would reject.
- * The first bytes hold arrival counters: zero the workspace once after
- * allocating it; every call leaves the counters zeroed again.  Calls that
- * share one workspace must be ordered on one stream.
+ * The first bytes hold arrival and completion counters: zero the workspace
+ * once after allocating it; every call leaves the counters zeroed again.
+ * Calls that share one workspace must be ordered on one stream.
+ *
+ * Merge scheduling.  When the whole grid of a call fits on the device at
+ * once, the blocks of a row wait for each other (for at most
+ * DCP_MERGE_WAIT_US microseconds, read from the environment at every call;
+ * default 30, 0 = never wait) so that each merges a share of the row; a
+ * block that stops waiting hands its share to the block that arrives last.
+ * The result is bit-identical either way.
  */
 size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
                                  int32_t num_shards, int64_t tokens_per_shard,

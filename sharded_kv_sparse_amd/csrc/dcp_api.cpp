@@ -2,6 +2,7 @@
 // dispatch to the HIP kernels.  Every check runs before anything is queued, so
 // a rejected call writes nothing.  No allocation, no synchronisation.
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
 
@@ -70,9 +71,10 @@ WorkspacePlan plan_workspace(long long rows, int heads, int num_shards, int spli
   w.needs_block_partials = want_merged || (want_partials && splits > 1);
   size_t off = 0;
   w.cnt_row_off = off;
-  if (want_merged) off += sizeof(int) * (size_t)rows;
+  const size_t hb = (size_t)(heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  if (want_merged) off += 2 * sizeof(int) * (size_t)rows * hb;      // per (row, head block)
   w.cnt_shard_off = off;
-  if (want_partials && splits > 1) off += sizeof(int) * (size_t)rows * num_shards;
+  if (want_partials && splits > 1) off += sizeof(int) * (size_t)rows * num_shards * hb;
   off = align256(off);
   w.ws_o_off = off;
   size_t blocks = (size_t)rows * num_shards * splits;
@@ -133,6 +135,34 @@ dcp_status check_common(const CommonArgs& a, bool dense) {
   return DCP_OK;
 }
 
+// Compute units of the current device (cached per device).
+long long device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kAssumedCUs;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kAssumedCUs;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Bound of the wait for the other blocks of a row before merging, in
+// 100 MHz ticks: DCP_MERGE_WAIT_US microseconds (default 30; 0 disables
+// waiting, so the last block to arrive merges the whole row).
+int merge_wait_ticks() {
+  const char* e = std::getenv("DCP_MERGE_WAIT_US");
+  long v = 30;
+  if (e && *e) {
+    char* end = nullptr;
+    const long x = std::strtol(e, &end, 10);
+    if (end != e && x >= 0 && x <= 100000) v = x;
+  }
+  return (int)(v * 100);
+}
+
 DecodeParams make_params(const CommonArgs& a, const WorkspacePlan& w) {
   DecodeParams p;
   std::memset(&p, 0, sizeof(p));
@@ -163,6 +193,9 @@ DecodeParams make_params(const CommonArgs& a, const WorkspacePlan& w) {
   }
   long long blocks = a.rows * a.num_shards * w.splits * p.head_blocks;
   p.xcd_swizzle = (blocks % 8 == 0) ? 1 : 0;
+  // The blocks of a row may wait for each other to share its merge only
+  // when the whole grid is resident at once (one block per compute unit).
+  p.merge_wait_ticks = blocks <= device_cus() ? merge_wait_ticks() : 0;
   return p;
 }
 

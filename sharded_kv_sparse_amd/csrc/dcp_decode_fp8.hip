@@ -19,13 +19,17 @@
 //     block scale (2^-e) undoes the power of two exactly.
 //
 // Data movement.  A tile is 128 tokens.  Its 576-byte rows are copied from
-// HBM straight into LDS with global->LDS DMA in a chunk-major layout,
-// [36 chunks of 16 bytes][128 token slots], one token per lane, so every
-// lane computes one row address per tile and the 18 copies it issues step
-// through that row 16 bytes at a time.  Two stages: tile it+1 streams in while tile it
-// is computed.  The slot ids (sparse) or page ids (dense) of tile it+2 are
-// DMA'd into a three-deep ring at the same time, so the row addresses of the
-// next tile are ready without a dependent global load.
+// HBM straight into LDS with global->LDS DMA.  Each copy instruction moves
+// one 64-byte granule of 16 tokens, four lanes per granule, so the global
+// side of every instruction is 16 whole 64-byte segments.  LDS layout of a
+// stage: [granule G: bytes 64G.. of the row, 9][token / 16][token % 16][4 x
+// 16-byte chunks], the chunks of token t permuted by XOR with sw(t) =
+// ((t >> 1) ^ (t >> 3) ^ (t >> 4)) & 3, which keeps the 16-byte operand
+// reads of S^T = K Q^T and the 8-byte transposing reads of V^T free of bank
+// conflicts on 32- and 64-bank LDS alike.  Two stages: tile it+1 streams in
+// while tile it is computed.  The slot ids (sparse) or page ids (dense) of
+// tile it+2 are DMA'd into a three-deep ring at the same time, so the row
+// addresses of the next tile are ready without a dependent global load.
 //
 // Per wave: 16 heads (4 waves = 64 heads; 128 heads use two blocks).  Per
 // tile: 8 S tiles x 5 k-steps x 2 (hi, lo) + 32 dim tiles x 3 (P' terms) =
@@ -39,33 +43,21 @@ namespace {
 
 constexpr int kT = 128;                            // tokens per tile
 constexpr int kRowBytes = 576;                     // E4M3 codes per key row
-constexpr int kChunks = 36;                        // 16-byte chunks per row
-constexpr int kPlane = kT * 16;                    // LDS bytes of one chunk plane
-constexpr int kTileBytes = kChunks * kPlane;       // 73728
+constexpr int kGranules = 9;                       // 64-byte granules per row
+constexpr int kGranPlane = kT * 64;                // LDS bytes of one granule plane
+constexpr int kTileBytes = kGranules * kGranPlane; // 73728
 constexpr int kStageBytes = kTileBytes + kT * 4;   // + per-token scales
 constexpr int kRingOff = 2 * kStageBytes;          // slot/page-id ring, 3 tiles
 constexpr int kSmem = kRingOff + 3 * kT * 4;       // 150016 bytes
 constexpr int kThreads = 256;
 
-// LDS slot of token t inside a chunk plane (an involution).  Tokens 16..31 of
-// every 32 swap 8-slot halves, so that the two 4-token groups one 16-lane
-// group gathers with a transposing read fall in different bank halves.
-__device__ __forceinline__ int slot_of(int t) { return t ^ (((t >> 4) & 1) << 3); }
+// Chunk permutation of token t inside its 64-byte granule.
+__device__ __forceinline__ int chunk_sw(int t) { return ((t >> 1) ^ (t >> 3) ^ (t >> 4)) & 3; }
 
 // Four E4M3 codes (RNE) of four floats, in byte order.
 __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
   int h = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, h, true);
-}
-
-// Largest e with x * 2^e <= 448 (the E4M3 maximum); 0 for x == 0.
-__device__ __forceinline__ int e4m3_exponent(float x) {
-  if (!(x > 0.f)) return 0;
-  int ex;
-  frexpf(448.0f / x, &ex);
-  int e = min(max(ex - 1, -120), 120);
-  while (e > -120 && ldexpf(x, e) > 448.0f) --e;
-  return e;
 }
 
 template <bool DENSE>
@@ -124,39 +116,100 @@ void decode_fp8_kernel(const DecodeParams p) {
     return min(max(r, 0), max_prow);
   };
 
-  // ---- ids of tiles 0 and 1 with plain loads (nothing else is in flight)
-  for (int i = tid; i < 2 * kT; i += kThreads) {
-    const int it = i / kT, t = i - it * kT;
-    if (it < ntiles) {
-      const int tok0 = start + it * kT;
-      const int nval = min(kT, end - tok0);
-      ring[it * kT + t] = *id_ptr(tok0 + (t < nval ? t : 0));
-    }
+  // ---- copies.  Rows of tile `it` into stage it & 1: wave w fills token
+  // groups 2w and 2w+1 (16 tokens each) for all 9 granules; lane l covers
+  // token 16(2w + h) + l/4 and the 16-byte chunk (l & 3) ^ sw of its granule.
+  // Waves 0 and 1 also copy the tile's 128 scales (token 64w + lane).
+  const int dma_tok = 32 * wave + (lane >> 2);     // + 16h
+  const int sc_tok = 64 * (wave & 1) + lane;
+  // Tokens past the tile's valid count re-read token 0 (never used).
+  auto eff = [&](int it, int t) { return t < min(kT, end - (start + it * kT)) ? t : 0; };
+  // A tile's copies are issued in pieces (copy c = 0..17: token group 2w +
+  // c / 9, granule c % 9) so that they can be spread over the MFMA work of
+  // the previous tile.
+  // Only the pool rows are kept between the copies (three registers); the
+  // addresses are formed at issue time.
+  struct RowCopies {
+    int prow[2];
+    int prow_sc;
+  };
+  const int chunk_off0 = 16 * ((lane & 3) ^ chunk_sw(dma_tok));
+  const int chunk_off1 = 16 * ((lane & 3) ^ chunk_sw(dma_tok + 16));
+  auto plan_rows = [&](int it, int id0, int id1, int idsc) {
+    RowCopies rc;
+    const int tok0 = start + it * kT;
+    rc.prow[0] = pool_row(tok0 + eff(it, dma_tok), id0);
+    rc.prow[1] = pool_row(tok0 + eff(it, dma_tok + 16), id1);
+    rc.prow_sc = pool_row(tok0 + eff(it, sc_tok), idsc);
+    return rc;
+  };
+  auto issue_copy = [&](const RowCopies& rc, int it, int c) {
+    const int h = c / kGranules, G = c - h * kGranules;
+    const char* src = kvbase + (long long)rc.prow[h] * kRowBytes + (h ? chunk_off1 : chunk_off0) + 64 * G;
+    dma16(src, smem + (it & 1) * kStageBytes + (2 * wave + h) * 1024 + G * kGranPlane);
+  };
+  auto issue_scales = [&](const RowCopies& rc, int it) {
+    if (wave < 2) dma4(sh.scale + rc.prow_sc, smem + (it & 1) * kStageBytes + kTileBytes + 256 * wave);
+  };
+  auto issue_rows = [&](int it, int id0, int id1, int idsc) {
+    const RowCopies rc = plan_rows(it, id0, id1, idsc);
+#pragma unroll
+    for (int c = 0; c < 2 * kGranules; ++c) issue_copy(rc, it, c);
+    issue_scales(rc, it);
+  };
+  // Ids of the tokens this lane copies in tile `it`, from the ring.
+  auto ring_ids = [&](int it, int& id0, int& id1, int& idsc) {
+    const DCP_LDS int* rg = ring + (it % 3) * kT;
+    id0 = rg[eff(it, dma_tok)];
+    id1 = rg[eff(it, dma_tok + 16)];
+    idsc = rg[eff(it, sc_tok)];
+  };
+  // Ids of tile `it` into ring slot it % 3 (waves 2 and 3, 64 tokens each).
+  auto issue_ring = [&](int it) {
+    const int t = (wave - 2) * 64 + lane;
+    dma4(id_ptr(start + it * kT + eff(it, t)), ring + (it % 3) * kT + (wave - 2) * 64);
+  };
+
+  // ---- tile 0's ids with plain loads (padding tokens re-read token 0)
+  int id0 = 0, id1 = 0, idsc = 0;
+  if (ntiles > 0) {
+    id0 = *id_ptr(start + eff(0, dma_tok));
+    id1 = *id_ptr(start + eff(0, dma_tok + 16));
+    idsc = *id_ptr(start + eff(0, sc_tok));
   }
+
+  // ---- query loads (consumed after tile 0's copies are queued)
+  const int head = hblk * kHeadsPerBlock + wave * 16 + i16;
+  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + head) * kHeadDim;
+  bf16x8 raw[5][4];
+#pragma unroll
+  for (int s = 0; s < 5; ++s)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int dim = 128 * s + 32 * g + 8 * u;
+      raw[s][u] = dim < kHeadDim ? *reinterpret_cast<const bf16x8*>(qrow + dim) : bf16x8{};
+    }
+  __builtin_amdgcn_sched_barrier(0);   // the query loads go out before the ids are waited for
+
+  if (ntiles > 0) issue_rows(0, id0, id1, idsc);
+  if (wave >= 2 && ntiles > 1) issue_ring(1);
 
   // ---- query: Q * 2^e as E4M3 hi + lo, k-step s covers dims 128s..128s+127
   // and lane group g holds dims 128s + 32g .. +32 (dims >= 576 are zero).
-  const int head = hblk * kHeadsPerBlock + wave * 16 + i16;
-  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + head) * kHeadDim;
   i32x8 qhi[5], qlo[5];
   float z_scale;
   {
-    bf16x8 raw[5][4];
     float qmax = 0.f;
 #pragma unroll
     for (int s = 0; s < 5; ++s)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int dim = 128 * s + 32 * g + 8 * u;
-        raw[s][u] = dim < kHeadDim ? *reinterpret_cast<const bf16x8*>(qrow + dim) : bf16x8{};
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[s][u][j])));
-      }
-    qmax = wave_xor_max(qmax, 16);
-    qmax = wave_xor_max(qmax, 32);
+    qmax = max_xor32(max_xor16(qmax));
     const int e = e4m3_exponent(qmax);
-    const float qs = ldexpf(1.0f, e);
-    z_scale = p.sm_scale_log2 * ldexpf(1.0f, -e);
+    const float qs = pow2i(e);
+    z_scale = p.sm_scale_log2 * pow2i(-e);
 #pragma unroll
     for (int s = 0; s < 5; ++s)
 #pragma unroll
@@ -175,33 +228,6 @@ void decode_fp8_kernel(const DecodeParams p) {
           qlo[s][2 * u + half] = l;
         }
   }
-  __syncthreads();   // ring slots 0 and 1 visible
-
-  // ---- copies.  Rows (and scales) of tile `it` into stage it & 1: wave w
-  // fills token slots 64*(w & 1) .. +63, one per lane, for chunk planes
-  // 18*(w >> 1) .. +17; waves 0 and 1 also copy the slots' scales.
-  auto issue_rows = [&](int it) {
-    DCP_LDS char* sb = smem + (it & 1) * kStageBytes;
-    const int h = wave & 1;
-    const int t = slot_of(64 * h + lane);          // token held in this lane's slot
-    const int tok0 = start + it * kT;
-    const int nval = min(kT, end - tok0);
-    const int tt = t < nval ? t : 0;               // padding re-reads token 0
-    const int prow = pool_row(tok0 + tt, ring[(it % 3) * kT + tt]);
-    const int c0 = 18 * (wave >> 1);
-    const char* src = kvbase + (long long)prow * kRowBytes + 16 * c0;
-    DCP_LDS char* dst = sb + c0 * kPlane + 1024 * h;
-#pragma unroll
-    for (int cc = 0; cc < 18; ++cc) dma16(src + 16 * cc, dst + cc * kPlane);
-    if (wave < 2) dma4(sh.scale + prow, sb + kTileBytes + 256 * h);
-  };
-  // Ids of tile `it` into ring slot it % 3 (waves 2 and 3, 64 tokens each).
-  auto issue_ring = [&](int it) {
-    const int t = (wave - 2) * 64 + lane;
-    const int tok0 = start + it * kT;
-    const int nval = min(kT, end - tok0);
-    dma4(id_ptr(tok0 + (t < nval ? t : 0)), ring + (it % 3) * kT + (wave - 2) * 64);
-  };
 
   // ---- online-softmax state; lane: head column, O^T dims 16d + 4g + i
   float m_run = kNegInf;    // reference max (base-2 logits), moves lazily
@@ -210,30 +236,45 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
   for (int d = 0; d < 32; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane LDS offsets (bytes) inside a stage
-  // QK: token 16st + i16 of S tile st sits in slot 16st + (i16 ^ 8(st & 1));
-  // lane group g reads chunks 8s + 2g and 8s + 2g + 1 (s = 4: g < 2 only).
-  const int qk_even = 2 * g * kPlane + 16 * i16;
-  const int qk_odd = 2 * g * kPlane + 16 * (i16 ^ 8);
-  const int qk4_even = 2 * (g & 1) * kPlane + 16 * i16;
-  const int qk4_odd = 2 * (g & 1) * kPlane + 16 * (i16 ^ 8);
+  // per-lane LDS offsets (bytes) inside a stage.
+  // QK: S tile st, k-step s < 4, lane (token i16, group g) reads chunks
+  // 2(g & 1) + cc (cc = 0, 1) of granule 2s + (g >> 1) of token 16st + i16;
+  // k-step 4 (RoPE dims 512..575, granule 8) the same chunks for g < 2.  The
+  // chunk permutation of token 16st + i16 is sw0(i16) ^ cst(st).
+  const int sw0 = ((i16 >> 1) ^ (i16 >> 3)) & 3;
+  int qk_lat[2][4], qk_rope[2][4];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int rel = 64 * i16 + 16 * ((2 * (g & 1) + cc) ^ sw0 ^ c);
+      qk_lat[cc][c] = (g >> 1) * kGranPlane + rel;
+      qk_rope[cc][c] = 8 * kGranPlane + rel;
+    }
   // PV: tr8 read r of lane L (group g) fetches token 32r + 16(jj >= 4) + 4g +
-  // (jj & 3), jj = L/2, bytes 8(L & 1) of a 16-byte chunk: lane i of the
-  // group then holds dim 16d + i of the 8 tokens of k-slots 8r..8r+7.
+  // (jj & 3), jj = L/2, bytes 8(L & 1) of chunk d & 3 of granule d >> 2: lane i
+  // of the group then holds dim 16d + i of the 8 tokens of k-slots 8r..8r+7.
+  // That token's chunk permutation is swl ^ 2(r & 1).
   const int jj = i16 >> 1;
-  const int pv_slot = (jj < 4) ? (4 * g + (jj & 3)) : (16 + ((4 * g + (jj & 3)) ^ 8));
-  const int pv_off = 16 * pv_slot + 8 * (i16 & 1);
-  // softmax: the scales of tokens 16st + 4g .. +3 sit in slots 16st + (4g ^ 8(st & 1)) ..
-  const int sc_even = 4 * (4 * g);
-  const int sc_odd = 4 * ((4 * g) ^ 8);
-
-  if (ntiles > 0) issue_rows(0);
+  const int pv_hi = jj >> 2, pv_p = 4 * g + (jj & 3);
+  const int swl = ((pv_p >> 1) ^ (pv_p >> 3) ^ (3 * pv_hi)) & 3;
+  int pv_off[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) pv_off[v] = 1024 * pv_hi + 64 * pv_p + 8 * (i16 & 1) + 16 * (v ^ swl);
+  // softmax: the scales of tokens 16st + 4g .. +3
+  const int sc_off = kTileBytes + 16 * g;
 
   for (int it = 0; it < ntiles; ++it) {
     wait_vmcnt<0>();
     lds_barrier();                       // tile it, its scales and ring(it + 1) landed
     if (wave >= 2 && it + 2 < ntiles) issue_ring(it + 2);
-    if (it + 1 < ntiles) issue_rows(it + 1);
+    const bool next = it + 1 < ntiles;
+    RowCopies rc{};
+    if (next) {
+      ring_ids(it + 1, id0, id1, idsc);
+      rc = plan_rows(it + 1, id0, id1, idsc);
+      for (int c = 0; c < 10; ++c) issue_copy(rc, it + 1, c);
+    }
 
     const DCP_LDS char* sb = smem + (it & 1) * kStageBytes;
     const int tok0 = start + it * kT;
@@ -249,11 +290,11 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int st = 4 * half + q;
-          const int base = (s < 4) ? ((st & 1) ? qk_odd : qk_even) + 8 * s * kPlane
-                                   : ((st & 1) ? qk4_odd : qk4_even) + 32 * kPlane;
-          const DCP_LDS char* rp = sb + base + 256 * st;
-          const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp);
-          const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp + kPlane);
+          const int cst = ((2 * st) ^ st) & 3;
+          const int o0 = (s < 4) ? qk_lat[0][cst] + 2 * s * kGranPlane : qk_rope[0][cst];
+          const int o1 = (s < 4) ? qk_lat[1][cst] + 2 * s * kGranPlane : qk_rope[1][cst];
+          const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + o0 + 1024 * st);
+          const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + o1 + 1024 * st);
           const bool live = (s < 4) || (g < 2);      // dims 576..639 are padding
           a[q] = live ? i32x8{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w} : i32x8{};
         }
@@ -271,6 +312,10 @@ void decode_fp8_kernel(const DecodeParams p) {
         for (int q = 0; q < 4; ++q)
           acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s & 1][q], qlo[s], acc[q], 0, 0,
                                                                    0, 127, 0, 127);
+        // next tile's copies, two per k-step, behind this step's MFMAs
+        {
+          const int slot = 5 * half + s;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -283,7 +328,7 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (DCP_LDS i32x2*)(sb + d * kPlane + 512 * r + pv_off));
+            (DCP_LDS i32x2*)(sb + (d >> 2) * kGranPlane + 2048 * r + pv_off[(d & 3) ^ (2 * (r & 1))]));
     };
 #pragma unroll
     for (int j = 0; j < 4; ++j) load_v(j, vr[0][j]);
@@ -295,8 +340,7 @@ void decode_fp8_kernel(const DecodeParams p) {
     float tmax = kNegInf;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(
-          sb + kTileBytes + 64 * st + ((st & 1) ? sc_odd : sc_even));
+      const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sc[st][i] = s4[i];
@@ -306,8 +350,7 @@ void decode_fp8_kernel(const DecodeParams p) {
         tmax = fmaxf(tmax, v);
       }
     }
-    tmax = wave_xor_max(tmax, 16);
-    tmax = wave_xor_max(tmax, 32);
+    tmax = max_xor32(max_xor16(tmax));
     const bool bump = tmax > m_run + 8.0f;
     if (__any(bump)) {
       const float m_new = bump ? tmax : m_run;
@@ -338,10 +381,9 @@ void decode_fp8_kernel(const DecodeParams p) {
     // operand layout lane group g holds k = 16g..16g+15 (bytes 0..15) and
     // 64+16g..64+16g+15 (bytes 16..31), while the scale of the 32-wide k block
     // kb is taken from lane group kb, so every scale block spans two groups.
-    pmax = wave_xor_max(pmax, 16);
-    pmax = wave_xor_max(pmax, 32);
+    pmax = max_xor32(max_xor16(pmax));
     const int ep = e4m3_exponent(pmax);
-    const float ps = ldexpf(1.0f, ep);
+    const float ps = pow2i(ep);
     const int pscale = 127 - ep;
     i32x8 p3[3];
 #pragma unroll
@@ -372,22 +414,29 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) load_v(4 * (grp + 1) + j, vr[(grp + 1) & 1][j]);
       }
+      i32x8 vt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const i32x2* r4 = vr[grp & 1][j];
-        const i32x8 vt = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
-        const int d = 4 * grp + j;
-#pragma unroll
-        for (int term = 0; term < 3; ++term)
-          oacc[d] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vt, p3[term], oacc[d], 0, 0, 0,
-                                                                    127, 0, pscale);
+        vt[j] = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
       }
+      if (next && grp < 4) {
+        issue_copy(rc, it + 1, 10 + 2 * grp);
+        issue_copy(rc, it + 1, 11 + 2 * grp);
+        if (grp == 3) issue_scales(rc, it + 1);
+      }
+      // term-major: four independent accumulators between dependent MFMAs
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          oacc[4 * grp + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              vt[j], p3[term], oacc[4 * grp + j], 0, 0, 0, 127, 0, pscale);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = sum_xor32(sum_xor16(l_run));
   finish_block<kThreads>(p, row, shard, split, head, g, true, oacc, m_run, l_tot, smem, &s_flag);
 }
 

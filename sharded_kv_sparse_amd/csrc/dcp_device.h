@@ -102,4 +102,65 @@ __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
+// Max with the value of lane ^ 16 and of lane ^ 32, through the gfx950 row
+// swaps (VALU only, no LDS round trip).  permlane16_swap exchanges the odd
+// 16-lane rows of its first operand with the even rows of its second, so
+// with both operands = v the pair holds {v[lane], v[lane ^ 16]} in some
+// order; permlane32_swap does the same for the two 32-lane halves.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 2^e as a float, for -126 <= e <= 127.
+__device__ __forceinline__ float pow2i(int e) { return __uint_as_float((unsigned)(e + 127) << 23); }
+
+// Largest e with x * 2^e <= 448 (the E4M3 maximum 1.75 * 2^8), clamped to
+// [-120, 120]; 0 when x is not positive.  From the bits of x = 1.m * 2^E:
+// e = 8 - E when 1.m <= 1.75 (mantissa field <= 0x600000), else 7 - E.
+__device__ __forceinline__ int e4m3_exponent(float x) {
+  const unsigned u = __float_as_uint(x);
+  const int E = (int)(u >> 23) - 127;
+  const int e = 8 - E - ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return x > 0.f ? min(max(e, -120), 120) : 0;
+}
+
+// Device-scope coherent global accesses.  Buffer loads and stores with the
+// SC1 cache-policy bit are the agent-scope forms of the gfx950 memory model
+// (those of relaxed agent-scope atomics), so data written this way by one
+// block is seen by a block on another XCD that reads it the same way after
+// an agent-scope atomic has ordered the two, with no L2 write-back or
+// invalidate.  A resource covers `bytes` bytes from `base`; offsets are in
+// bytes and out-of-range accesses read 0 / are dropped.
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ float load_coherent(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 v) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCachePolicySc1);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kCachePolicySc1);
+}
+
 }  // namespace dcp

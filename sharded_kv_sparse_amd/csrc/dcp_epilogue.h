@@ -1,5 +1,5 @@
 // Epilogue shared by the decode kernels: per-block partial output, arrival
-// counters and the LSE merge done by the last block of a row (the pack and
+// counters and the LSE merge of a (row, head block)'s partials (the pack and
 // combine steps fused into the attention kernel).
 //
 // Merge ([P1] "feat: support decode context parallelism for PyTorch MLA",
@@ -9,6 +9,27 @@
 // flashmla_kv backend", review of the LSE combine): M = max LSE_r over
 // partials with LSE_r > -inf, O = sum_r e^(LSE_r - M) O_r / sum_r e^(LSE_r - M),
 // LSE = M + ln sum; O = 0 and LSE = -inf when every partial is empty.
+//
+// Hand-off between blocks.  Every block stores its normalised partial with
+// device-scope coherent stores (agent-scope relaxed-atomic form of the
+// gfx950 memory model: written through to memory, so no L2 write-back is
+// needed), waits for them, and then counts itself on the agent-scope
+// arrival word of its (row, head block).  The workspace copy of a partial
+// is laid out [dim tile d][head][lane group g][4 dims], so that the 64 lanes
+// of a wave store -- and a merger loads -- 1 KB contiguous per instruction.
+//
+// The merge is split into n_in parts of the head block's elements, one per
+// member (partial).  When the grid fits on the GPU at once, a block that is
+// not the last to arrive waits (bounded in time) for the others and then
+// merges its own part, so the merge of a row runs on all its blocks in
+// parallel.  A block that gives up first marks its part abandoned, with a
+// compare-and-swap that can only succeed before the last arrival; the last
+// arriver merges its own part plus every abandoned one.  Without waiting
+// (large grids, many partials, or a zero time limit) every block arrives
+// with its part marked abandoned, and the last arriver merges everything.
+// Partials are added in index order, so the result does not depend on
+// which block merges.  The block that completes the last part resets the
+// arrival and completion words, so the workspace needs zeroing only once.
 #pragma once
 
 #include "dcp_device.h"
@@ -16,154 +37,218 @@
 
 namespace dcp {
 
-// Block-wide LSE merge of n_in partials [n_in][H][512] + [n_in][H] into one
-// [H][512] output (fp32 or bf16) + [H] LSE.  Weights go to LDS first; then
-// every thread merges float4 columns with all of its loads for a batch of
-// inputs issued before any is consumed, so the merge is bandwidth- rather
-// than latency-bound.  A partial whose weight is 0 (empty shard) is loaded
-// but never multiplied: the select keeps NaN garbage out.
+constexpr int kMaxWaitMembers = 24;         // abandon bits 8..31 of the arrival word
+
+// Weights of the n_in partials of a head block, from their LSEs: w[i][hl]
+// (normalised), and the merged LSE of each head written to out_lse when
+// asked.  Whole block; leaves w in LDS.
 template <int NT>
-__device__ inline void merge_partials(const float* __restrict__ in_o, const float* __restrict__ in_lse,
-                               int n_in, int H, void* __restrict__ out_o, int out_bf16,
-                               float* __restrict__ out_lse, DCP_LDS float* wts) {
-  const int tid = threadIdx.x;
-  for (int h = tid; h < H; h += NT) {
-    float m = kNegInf;
-    for (int i = 0; i < n_in; ++i) {
-      float l = __builtin_nontemporal_load(in_lse + (size_t)i * H + h);
-      m = (l > m) ? l : m;
-    }
-    float wsum = 0.f;
-    for (int i = 0; i < n_in; ++i) {
-      float l = __builtin_nontemporal_load(in_lse + (size_t)i * H + h);
-      float w = (m > kNegInf && l > kNegInf) ? fast_exp2((l - m) * kLog2e) : 0.f;
-      wts[i * H + h] = w;
-      wsum += w;
-    }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    for (int i = 0; i < n_in; ++i) wts[i * H + h] *= inv;
-    out_lse[h] = wsum > 0.f ? m + logf(wsum) : kNegInf;
+__device__ inline void merge_weights(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
+                                     float* out_lse, bool write_lse, DCP_LDS float* w) {
+  const int H = p.heads, tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(p.ws_lse + part0 * H, (unsigned)(n_in * H) * 4u);
+  for (int i = tid; i < n_in * nh; i += NT) {
+    const int pi = i / nh, hl = i - pi * nh;
+    w[pi * kHeadsPerBlock + hl] = load_coherent(rl, (unsigned)(pi * H + h0 + hl) * 4u);
   }
   __syncthreads();
-  constexpr int C = kVDim / 4;
-  constexpr int B = 8;                 // inputs loaded per batch
-  constexpr int CH = 2;                // columns per thread per pass
-  const f32x4* src = reinterpret_cast<const f32x4*>(in_o);
-  for (int base = tid; base < H * C; base += NT * CH) {
-    f32x4 acc[CH];
-    int hh[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      hh[u] = min(base + u * NT, H * C - 1) / C;
+  for (int hl = tid; hl < nh; hl += NT) {
+    float M = kNegInf;
+    for (int i = 0; i < n_in; ++i) M = fmaxf(M, w[i * kHeadsPerBlock + hl]);
+    float sum = 0.f;
+    for (int i = 0; i < n_in; ++i) {
+      const float l = w[i * kHeadsPerBlock + hl];
+      const float e = (M > kNegInf && l > kNegInf) ? fast_exp2((l - M) * kLog2e) : 0.f;
+      w[i * kHeadsPerBlock + hl] = e;
+      sum += e;
     }
-    for (int i0 = 0; i0 < n_in; i0 += B) {
-      f32x4 v[CH][B];
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    for (int i = 0; i < n_in; ++i) w[i * kHeadsPerBlock + hl] *= inv;
+    if (write_lse) out_lse[h0 + hl] = sum > 0.f ? M + logf(sum) : kNegInf;
+  }
+  __syncthreads();
+}
+
+// Merges part `part` of `n_parts` of the head block's 128 * nh float4
+// elements (element e: dim tile e / 4nh, head (e / 4) % nh, lane group e % 4)
+// over the partials part0 .. part0 + n_in - 1 into out (the output row's
+// [H][512] values, fp32 or bf16).  Whole block.
+template <int NT>
+__device__ inline void merge_part(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
+                                  int part, int n_parts, const DCP_LDS float* w, void* out,
+                                  int out_bf16) {
+  const int H = p.heads, tid = threadIdx.x;
+  const int T = 128 * nh;
+  const int e0 = (int)((long long)part * T / n_parts), e1 = (int)((long long)(part + 1) * T / n_parts);
+  const unsigned part_bytes = (unsigned)H * kVDim * 4u;
+  const __amdgpu_buffer_rsrc_t ro =
+      coherent_rsrc(p.ws_o + part0 * H * kVDim, (unsigned)n_in * part_bytes);
+  const unsigned blk_off = (unsigned)h0 * kVDim * 4u;
+  constexpr unsigned kNowhere = 0x80000000u;      // beyond every resource: reads 0, no traffic
+  constexpr int K = 8;                             // elements per thread per pass
+  for (int eb = e0; eb < e1; eb += NT * K) {
+    f32x4 acc[K];
+    int hl[K];
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int idx = min(base + u * NT, H * C - 1);
+    for (int k = 0; k < K; ++k) {
+      acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int e = min(eb + k * NT + tid, e1 - 1);
+      hl[k] = (e >> 2) % nh;
+    }
+    for (int i0 = 0; i0 < n_in; i0 += 4) {
+      f32x4 v[4][K];
 #pragma unroll
-        for (int j = 0; j < B; ++j) {
-          const int i = min(i0 + j, n_in - 1);
-          v[u][j] = __builtin_nontemporal_load(src + (size_t)i * H * C + idx);
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int e = eb + k * NT + tid;
+          const bool live = i0 + u < n_in && e < e1;
+          v[u][k] = load_coherent4(ro, live ? (unsigned)(i0 + u) * part_bytes + blk_off + 16u * e : kNowhere);
         }
-      }
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int j = 0; j < B; ++j) {
-          const float w = (i0 + j < n_in) ? wts[(i0 + j) * H + hh[u]] : 0.f;
-          acc[u] += (w != 0.f) ? w * v[u][j] : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < K; ++k) {
+          const float wt = i0 + u < n_in ? w[(i0 + u) * kHeadsPerBlock + hl[k]] : 0.f;
+          acc[k] += (wt != 0.f) ? wt * v[u][k] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      }
     }
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = base + u * NT;
-      if (idx >= H * C) break;
+    for (int k = 0; k < K; ++k) {
+      const int e = eb + k * NT + tid;
+      if (e >= e1) break;
+      const int d = e / (4 * nh), g = e & 3;
+      const size_t idx = (size_t)(h0 + hl[k]) * kVDim + 16 * d + 4 * g;
       if (out_bf16) {
-        unsigned lo = f32_to_bf16_bits(acc[u][0]) | ((unsigned)f32_to_bf16_bits(acc[u][1]) << 16);
-        unsigned hi = f32_to_bf16_bits(acc[u][2]) | ((unsigned)f32_to_bf16_bits(acc[u][3]) << 16);
-        reinterpret_cast<uint2*>(out_o)[idx] = make_uint2(lo, hi);
+        const unsigned lo = f32_to_bf16_bits(acc[k][0]) | ((unsigned)f32_to_bf16_bits(acc[k][1]) << 16);
+        const unsigned hi = f32_to_bf16_bits(acc[k][2]) | ((unsigned)f32_to_bf16_bits(acc[k][3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<unsigned short*>(out) + idx) = make_uint2(lo, hi);
       } else {
-        reinterpret_cast<f32x4*>(out_o)[idx] = acc[u];
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = acc[k];
       }
     }
   }
 }
 
 // Writes this block's normalised partial (O / l and LSE = ln l + max) for
-// its heads to the workspace and/or o_part, then elects the last block of
-// the (row, shard) and of the row with arrival counters and merges there.
-// Release: all stores issued, workgroup barrier, device fence, count.
-// Acquire: the winner fences again before reading the others' partials.
-// The winner resets the counter, so the workspace needs zeroing only once.
-// oacc[d][i] holds O^T for dim 16d + 4g + i of `head`; m_run / l_tot are the
-// head's base-2 reference max and its sum of 2^(z - m_run).
+// its heads to the workspace and/or o_part, then takes part in the merges of
+// its (row, shard, head block) (splits -> o_part) and (row, head block)
+// (everything -> o).  oacc[d][i] holds O^T for dim 16d + 4g + i of `head`;
+// m_run / l_tot are the head's base-2 reference max and its sum of
+// 2^(z - m_run).
 template <int NT>
 __device__ inline void finish_block(const DecodeParams& p, long long row, int shard, int split,
                                     int head, int g, bool writer, const f32x4 (&oacc)[32],
                                     float m_run, float l_tot, DCP_LDS char* smem, int* s_flag) {
   const int tid = threadIdx.x;
   const int N = p.num_shards, S = p.num_splits, HB = p.head_blocks, H = p.heads;
+  const int hblk = head / kHeadsPerBlock;
+  const int h0 = hblk * kHeadsPerBlock, nh = min(kHeadsPerBlock, H - h0), hl = head - h0;
   const bool need_shard_merge = p.o_part != nullptr && S > 1;
   const bool fused = p.o != nullptr;
   const bool to_ws = fused || need_shard_merge;
   const bool to_part = p.o_part != nullptr && S == 1;
+
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+  const long long blk_part = (row * N + shard) * S + split;
   if (writer) {
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
-    const long long blk_part = ((row * N + shard) * S + split);
-    float* wo = to_ws ? p.ws_o + (blk_part * H + head) * kVDim : nullptr;
-    float* po = to_part ? p.o_part + (((long long)shard * p.rows + row) * H + head) * kVDim : nullptr;
+    if (to_part) {
+      float* po = p.o_part + (((long long)shard * p.rows + row) * H + head) * kVDim;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const f32x4 v = oacc[d] * inv;
-      const int dim = 16 * d + 4 * g;
-      if (to_ws) *reinterpret_cast<f32x4*>(wo + dim) = v;
-      if (to_part) *reinterpret_cast<f32x4*>(po + dim) = v;
+      for (int d = 0; d < 32; ++d) *reinterpret_cast<f32x4*>(po + 16 * d + 4 * g) = oacc[d] * inv;
+      if (g == 0) p.lse_part[((long long)shard * p.rows + row) * H + head] = lse_v;
     }
-    if (g == 0) {
-      if (to_ws) p.ws_lse[blk_part * H + head] = lse_v;
-      if (to_part) p.lse_part[((long long)shard * p.rows + row) * H + head] = lse_v;
+    if (to_ws) {
+      const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(p.ws_o + (blk_part * H + h0) * kVDim,
+                                                      (unsigned)nh * kVDim * 4u);
+#pragma unroll
+      for (int d = 0; d < 32; ++d)
+        store_coherent4(ro, (unsigned)((d * nh + hl) * 4 + g) * 16u, oacc[d] * inv);
+      if (g == 0) store_coherent(coherent_rsrc(p.ws_lse + blk_part * H, (unsigned)H * 4u),
+                                 (unsigned)head * 4u, lse_v);
     }
   }
   if (!to_ws) return;
 
-  __syncthreads();
-  DCP_LDS float* wts = (DCP_LDS float*)smem;
+  wait_vmcnt<0>();       // this thread's coherent stores have completed ...
+  __syncthreads();       // ... and so have those of every thread of the block
+  DCP_LDS float* w = (DCP_LDS float*)smem;                    // [kMaxMergeInputs][64]
+  DCP_LDS unsigned* s_word = (DCP_LDS unsigned*)(w + kMaxMergeInputs * kHeadsPerBlock);
+
   if (need_shard_merge) {
-    if (tid == 0) {
-      __threadfence();
-      const int old = atomicAdd(p.cnt_shard + row * N + shard, 1);
-      *s_flag = (old == S * HB - 1);
-    }
+    // splits of one shard -> o_part: the last of the S blocks merges
+    int* cnt = p.cnt_shard + (row * N + shard) * HB + hblk;
+    if (tid == 0)
+      *s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
     __syncthreads();
     if (*s_flag) {
-      __threadfence();
-      const long long base = (row * N + shard) * S;
-      merge_partials<NT>(p.ws_o + base * H * kVDim, p.ws_lse + base * H, S, H,
-                         p.o_part + ((long long)shard * p.rows + row) * H * kVDim, 0,
-                         p.lse_part + ((long long)shard * p.rows + row) * H, wts);
-      if (tid == 0) p.cnt_shard[row * N + shard] = 0;
+      const long long part0 = (row * N + shard) * S;
+      merge_weights<NT>(p, part0, S, h0, nh, p.lse_part + ((long long)shard * p.rows + row) * H, true, w);
+      merge_part<NT>(p, part0, S, h0, nh, 0, 1, w,
+                     p.o_part + ((long long)shard * p.rows + row) * H * kVDim, 0);
+      if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
   }
-  if (fused) {
-    if (tid == 0) {
-      __threadfence();
-      const int old = atomicAdd(p.cnt_row + row, 1);
-      *s_flag = (old == N * S * HB - 1);
+  if (!fused) return;
+
+  // ---- all partials of the row -> o.  Arrival word: count in bits 0..7,
+  // abandoned parts in bits 8 + member.  Completion word: parts merged.
+  const int n_in = N * S, member = shard * S + split;
+  unsigned* arrive = reinterpret_cast<unsigned*>(p.cnt_row + (row * HB + hblk) * 2);
+  unsigned* done = arrive + 1;
+  const bool may_wait = p.merge_wait_ticks > 0 && n_in <= kMaxWaitMembers;
+  if (tid == 0) {
+    const unsigned add = 1u + (!may_wait && n_in <= kMaxWaitMembers ? 1u << (8 + member) : 0u);
+    const unsigned old = __hip_atomic_fetch_add(arrive, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned parts = 0u;                 // bit 0: own part; bit 1: last arriver
+    if ((old & 0xffu) == (unsigned)n_in - 1) {
+      parts = 3u;
+      s_word[1] = old;
+    } else if (may_wait) {
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        const unsigned now = __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((now & 0xffu) == (unsigned)n_in) { parts = 1u; break; }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)p.merge_wait_ticks) {
+          unsigned expect = now;
+          if (__hip_atomic_compare_exchange_strong(arrive, &expect, now | (1u << (8 + member)),
+                                                   __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;                       // abandoned: the last arriver merges this part
+          continue;                      // the word moved; look again
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
     }
-    __syncthreads();
-    if (*s_flag) {
-      __threadfence();
-      const long long base = row * N * S;
-      void* out = p.out_bf16 ? (void*)(static_cast<unsigned short*>(p.o) + row * H * kVDim)
-                             : (void*)(static_cast<float*>(p.o) + row * H * kVDim);
-      merge_partials<NT>(p.ws_o + base * H * kVDim, p.ws_lse + base * H, N * S, H, out,
-                         p.out_bf16, p.lse + row * H, wts);
-      if (tid == 0) p.cnt_row[row] = 0;
+    s_word[0] = parts;
+  }
+  __syncthreads();
+  const unsigned parts = s_word[0];
+  if (parts == 0u) return;
+  // The last arriver merges every part whose member gave up (all parts
+  // when there are too many members for abandon bits).
+  const bool all = (parts & 2u) && n_in > kMaxWaitMembers;
+  const unsigned abandoned = (parts & 2u) ? (s_word[1] >> 8) : 0u;
+
+  void* out = p.out_bf16 ? (void*)(static_cast<unsigned short*>(p.o) + row * H * kVDim)
+                         : (void*)(static_cast<float*>(p.o) + row * H * kVDim);
+  const long long part0 = row * N * S;
+  merge_weights<NT>(p, part0, n_in, h0, nh, p.lse + row * H, (parts & 2u) != 0u, w);
+  int merged = 0;
+  for (int m = 0; m < n_in; ++m) {
+    if (!(all || m == member || (m < kMaxWaitMembers && ((abandoned >> m) & 1u)))) continue;
+    merge_part<NT>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
+    ++merged;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(done, (unsigned)merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + (unsigned)merged == (unsigned)n_in) {
+      __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -51,9 +51,10 @@ struct DecodeParams {
   // workspace
   float* ws_o;                   // [rows, N, S, heads, 512]
   float* ws_lse;                 // [rows, N, S, heads]
-  int* cnt_row;                  // [rows]
-  int* cnt_shard;                // [rows, N]
+  int* cnt_row;                  // [rows, head blocks, 2]: arrival and completion words
+  int* cnt_shard;                // [rows, N, head blocks]
   int xcd_swizzle;               // grid is a multiple of 8: keep a row's blocks on one XCD
+  int merge_wait_ticks;          // >0: blocks wait up to this many 100 MHz ticks to share a merge
 };
 
 // Workspace plan shared by the size query and the decode calls.

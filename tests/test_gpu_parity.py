@@ -208,10 +208,39 @@ def test_fused_equals_unfused_and_counters_reset(gpu):
     o_c, lse_c = B.lse_combine(parts["o_part"], parts["lse_part"])
     torch.cuda.synchronize()
     assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
-    assert (ws[: 4 * p.rows].view(torch.int32) == 0).all()
+    hb = (p.heads + 63) // 64
+    assert (ws[: 8 * p.rows * hb].view(torch.int32) == 0).all()    # arrival + completion words
     np.testing.assert_allclose(to_np(a["o"]), to_np(o_c), rtol=0, atol=1e-5)
     np.testing.assert_allclose(to_np(a["lse"]), to_np(lse_c), rtol=0, atol=1e-5)
     check_against_oracle(a, oracle_sparse(w), "fused")
+
+
+@pytest.mark.parametrize("name", ["sparse_fp8_b64_k2048", "sparse_bf16_b8_k2048"])
+def test_fused_merge_modes_agree(gpu, name, monkeypatch):
+    # The row's blocks share the merge (bounded wait), give up at once (1 us),
+    # or never wait (the last block merges everything): bit-identical results,
+    # counters back at zero every time, and within tolerance of the oracle.
+    p = wl.preset(name)
+    w = make(p)
+    table = w.dev(w.table)
+    local, counts = B.remap_topk(table, p.num_shards)
+    nb = B.workspace_size(False, p.rows, p.heads, p.num_shards, p.topk, want_merged=True,
+                          want_partials=False)
+    ws = B.alloc_workspace(nb, gpu)
+    hb = (p.heads + 63) // 64
+    res = {}
+    for us in ["30", "1", "0", "30"]:
+        say(f"merge wait {us} us")
+        monkeypatch.setenv("DCP_MERGE_WAIT_US", us)
+        r = B.sparse_decode(w.q, w.pools[0], w.scales[0], local, counts, p.sigma, workspace=ws)
+        torch.cuda.synchronize()
+        assert (ws[: 8 * p.rows * hb].view(torch.int32) == 0).all()
+        if us in res:
+            assert torch.equal(r["o"], res[us]["o"]) and torch.equal(r["lse"], res[us]["lse"])
+        res[us] = r
+    for us in ["1", "0"]:
+        assert torch.equal(res[us]["o"], res["30"]["o"]) and torch.equal(res[us]["lse"], res["30"]["lse"])
+    check_against_oracle(res["30"], oracle_sparse(w), f"{name} fused")
 
 
 def test_bf16_output(gpu):
