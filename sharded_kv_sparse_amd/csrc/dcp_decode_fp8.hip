@@ -20,20 +20,21 @@
 //
 // Data movement.  A tile is 128 tokens.  Its 576-byte rows are copied from
 // HBM straight into LDS with global->LDS DMA.  Each copy instruction moves
-// one 64-byte granule of 16 tokens, four lanes per granule, so the global
-// side of every instruction is 16 whole 64-byte segments.  LDS layout of a
+// one 64-byte granule of 16 tokens, four lanes per granule.  LDS layout of a
 // stage: [granule G: bytes 64G.. of the row, 9][token / 16][token % 16][4 x
 // 16-byte chunks], the chunks of token t permuted by XOR with sw(t) =
 // ((t >> 1) ^ (t >> 3) ^ (t >> 4)) & 3, which keeps the 16-byte operand
 // reads of S^T = K Q^T and the 8-byte transposing reads of V^T free of bank
-// conflicts on 32- and 64-bank LDS alike.  Two stages: tile it+1 streams in
-// while tile it is computed.  The slot ids (sparse) or page ids (dense) of
-// tile it+2 are DMA'd into a three-deep ring at the same time, so the row
-// addresses of the next tile are ready without a dependent global load.
+// conflicts on 32- and 64-bank LDS alike; then the tile's 128 fp32 token
+// scales.  Two stages: tile it+1 streams in while tile it is computed, its
+// copies issued among the QK MFMAs of tile it.  The slot ids (sparse) or
+// page ids (dense) of tile it+2 are DMA'd into a three-deep ring at the same
+// time, so the row addresses of the next tile are ready without a dependent
+// global load.
 //
 // Per wave: 16 heads (4 waves = 64 heads; 128 heads use two blocks).  Per
-// tile: 8 S tiles x 5 k-steps x 2 (hi, lo) + 32 dim tiles x 3 (P' terms) =
-// 176 MFMAs of 16x16x128.
+// tile: 8 S tiles x (4 latent k-steps x 2 (hi, lo) + 1 RoPE k-step) + 32 dim
+// tiles x 3 (P' terms) = 168 MFMAs of 16x16x128.
 #include "dcp_device.h"
 #include "dcp_epilogue.h"
 #include "dcp_internal.h"
@@ -103,7 +104,8 @@ void decode_fp8_kernel(const DecodeParams p) {
   }
   n_tok = max(n_tok, 0);
   const int chunk = ((n_tok + S - 1) / S + kT - 1) / kT * kT;
-  const int start = min(n_tok, split * chunk);
+  // (split 0 starts at 0 without waiting for the count)
+  const int start = split == 0 ? 0 : min(n_tok, split * chunk);
   const int end = min(n_tok, start + chunk);
   const int ntiles = (end - start + kT - 1) / kT;
 
@@ -124,29 +126,33 @@ void decode_fp8_kernel(const DecodeParams p) {
   // Waves 0 and 1 also copy the tile's 128 scales (token 64w + lane).
   const int dma_tok = 32 * wave + (lane >> 2);     // + 16h
   const int sc_tok = 64 * (wave & 1) + lane;
-  // Tokens past the tile's valid count re-read token 0 (never used).
+  // Tokens past the tile's valid count copy the tile's first token: they are
+  // masked out of the softmax, and a real row keeps their V codes finite
+  // (P' = 0 times a NaN code would still be NaN).
   auto eff = [&](int it, int t) { return t < min(kT, end - (start + it * kT)) ? t : 0; };
-  // A tile's copies are issued in pieces (copy c = 0..17: token group 2w +
-  // c / 9, granule c % 9) so that they can be spread over the MFMA work of
-  // the previous tile.
-  // Only the pool rows are kept between the copies (three registers); the
-  // addresses are formed at issue time.
+  // A tile's copies are issued in pieces (copy c = 0..17: granule c / 2 of
+  // token group 2w + (c & 1), granule-major) so that they can be spread over
+  // the MFMA work of the previous tile and the next tile's first k-steps can
+  // start on the first granules.  Only the pool rows are kept between the
+  // copies (three registers); the addresses are formed at issue time.
   struct RowCopies {
     int prow[2];
     int prow_sc;
   };
+  struct TileIds {
+    int id[2];
+    int sc;
+  };
   const int chunk_off0 = 16 * ((lane & 3) ^ chunk_sw(dma_tok));
   const int chunk_off1 = 16 * ((lane & 3) ^ chunk_sw(dma_tok + 16));
-  auto plan_rows = [&](int it, int id0, int id1, int idsc) {
+  auto plan_rows = [&](int it, const TileIds& id) {
     RowCopies rc;
     const int tok0 = start + it * kT;
-    rc.prow[0] = pool_row(tok0 + eff(it, dma_tok), id0);
-    rc.prow[1] = pool_row(tok0 + eff(it, dma_tok + 16), id1);
-    rc.prow_sc = pool_row(tok0 + eff(it, sc_tok), idsc);
+    rc.prow[0] = pool_row(tok0 + eff(it, dma_tok), id.id[0]);
+    rc.prow[1] = pool_row(tok0 + eff(it, dma_tok + 16), id.id[1]);
+    rc.prow_sc = pool_row(tok0 + eff(it, sc_tok), id.sc);
     return rc;
   };
-  // Copy c of a tile: granule c / 2 of token group 2w + (c & 1) (granule-major,
-  // so that the k-steps of the next tile can start on the first granules).
   auto issue_copy = [&](const RowCopies& rc, int it, int c) {
     const int h = c & 1, G = c >> 1;
     const char* src = kvbase + (long long)rc.prow[h] * kRowBytes + (h ? chunk_off1 : chunk_off0) + 64 * G;
@@ -155,18 +161,12 @@ void decode_fp8_kernel(const DecodeParams p) {
   auto issue_scales = [&](const RowCopies& rc, int it) {
     if (wave < 2) dma4(sh.scale + rc.prow_sc, smem + (it & 1) * kStageBytes + kTileBytes + 256 * wave);
   };
-  auto issue_rows = [&](int it, int id0, int id1, int idsc) {
-    const RowCopies rc = plan_rows(it, id0, id1, idsc);
-#pragma unroll
-    for (int c = 0; c < 2 * kGranules; ++c) issue_copy(rc, it, c);
-    issue_scales(rc, it);
-  };
   // Ids of the tokens this lane copies in tile `it`, from the ring.
-  auto ring_ids = [&](int it, int& id0, int& id1, int& idsc) {
+  auto ring_ids = [&](int it, TileIds& id) {
     const DCP_LDS int* rg = ring + (it % 3) * kT;
-    id0 = rg[eff(it, dma_tok)];
-    id1 = rg[eff(it, dma_tok + 16)];
-    idsc = rg[eff(it, sc_tok)];
+    id.id[0] = rg[eff(it, dma_tok)];
+    id.id[1] = rg[eff(it, dma_tok + 16)];
+    id.sc = rg[eff(it, sc_tok)];
   };
   // Ids of tile `it` into ring slot `slot` (waves 2 and 3, 64 tokens each).
   auto issue_ring_slot = [&](int it, int slot) {
@@ -174,17 +174,23 @@ void decode_fp8_kernel(const DecodeParams p) {
     dma4(id_ptr(start + it * kT + eff(it, t)), ring + slot * kT + (wave - 2) * 64);
   };
 
-  // ---- tile 0's ids with plain loads (padding tokens re-read token 0)
-  int id0 = 0, id1 = 0, idsc = 0;
-  if (ntiles > 0) {
-    id0 = *id_ptr(start + eff(0, dma_tok));
-    id1 = *id_ptr(start + eff(0, dma_tok + 16));
-    idsc = *id_ptr(start + eff(0, sc_tok));
-  }
+  // ---- tile 0's ids.  For split 0 their loads do not wait for the count:
+  // they are bounded by the id table (cap entries) instead, and the ids of
+  // tokens past the count are replaced by the first token's once the count
+  // is known, when the copies are planned.
+  const int cap = DENSE ? p.max_pages * p.page_size : p.k;
+  const __amdgpu_buffer_rsrc_t id_rsrc =
+      coherent_rsrc(ids, (unsigned)(DENSE ? p.max_pages : p.k) * 4u);
+  auto id_at = [&](int j) { return load_bounded(id_rsrc, (unsigned)(DENSE ? j / page : j) * 4u); };
+  auto tok_cap = [&](int t) { return start + t < cap ? t : 0; };
+  TileIds ids0;
+  ids0.id[0] = id_at(start + tok_cap(dma_tok));
+  ids0.id[1] = id_at(start + tok_cap(dma_tok + 16));
+  ids0.sc = id_at(start + tok_cap(sc_tok));
+  const int id_first = id_at(start);
 
-  // ---- query loads (consumed after tile 0's copies are queued).  Latent
-  // k-step s < 4: lane group g holds dims 128s + 32g .. +32; RoPE: dims
-  // 512 + 16g .. +16.
+  // ---- query loads.  Latent k-step s < 4: lane group g holds dims 128s +
+  // 32g .. +32; RoPE: dims 512 + 16g .. +16.
   const int head = hblk * kHeadsPerBlock + wave * 16 + i16;
   const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + head) * kHeadDim;
   bf16x8 raw[4][4], raw_r[2];
@@ -195,10 +201,39 @@ void decode_fp8_kernel(const DecodeParams p) {
       raw[s][u] = *reinterpret_cast<const bf16x8*>(qrow + 128 * s + 32 * g + 8 * u);
 #pragma unroll
   for (int u = 0; u < 2; ++u) raw_r[u] = *reinterpret_cast<const bf16x8*>(qrow + 512 + 16 * g + 8 * u);
-  __builtin_amdgcn_sched_barrier(0);   // the query loads go out before the ids are waited for
+  // The query and the ids are waited for here, before any copy is queued: the waits the
+  // compiler places before the first use of a load do not count the copies
+  // (inline global->LDS instructions), so a use after them would also wait
+  // for every copy of tile 0.
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) touch(raw[s][u]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) touch(raw_r[u]);
+  touch(ids0.id[0]);
+  touch(ids0.id[1]);
+  touch(ids0.sc);
+  touch(id_first);
 
-  if (ntiles > 0) issue_rows(0, id0, id1, idsc);
-  if (wave >= 2 && ntiles > 1) issue_ring_slot(1, 1);
+  // ---- tile 0: the scales (waves 0, 1) or the ids of tile 1 (waves 2, 3)
+  // first, as at the top of every tile, then granules 0..3 (copies 0..7);
+  // the rest follows the query split below.
+  const bool issue0 = ntiles > 0, ring1 = ntiles > 1;
+  {
+    auto valid0 = [&](int t) { return start + t < end; };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ids0.id[h] = valid0(dma_tok + 16 * h) ? ids0.id[h] : id_first;
+    ids0.sc = valid0(sc_tok) ? ids0.sc : id_first;
+  }
+  const RowCopies rc0 = plan_rows(0, ids0);
+  if (issue0 && wave < 2) issue_scales(rc0, 0);
+  if (wave >= 2 && ring1) issue_ring_slot(1, 1);
+  if (issue0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) issue_copy(rc0, 0, c);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- query: Q * 2^e as E4M3 hi + lo (e per head: the largest with
   // max |Q| * 2^e <= 448; a bf16 value has 8 significant bits, so hi + lo is
@@ -256,6 +291,11 @@ void decode_fp8_kernel(const DecodeParams p) {
     for (int s = 0; s < 4; ++s) asm volatile("" : "+a"(qhi[s]), "+a"(qlo[s]));
     asm volatile("" : "+a"(qr));
   }
+  __builtin_amdgcn_sched_barrier(0);
+  if (issue0) {
+#pragma unroll
+    for (int c = 8; c < 18; ++c) issue_copy(rc0, 0, c);
+  }
 
   // ---- online-softmax state; lane: head column, O^T dims 16d + 4g + i.
   // Logits are kept as y = q.k * scale_t; the base-2 logit is c * y.
@@ -296,39 +336,50 @@ void decode_fp8_kernel(const DecodeParams p) {
 
   // Copy schedule of tile it + 1 while tile it is computed (per wave, in
   // this order): one 4-byte copy at the top (scales of it + 1 on waves 0, 1;
-  // ids of it + 2 on waves 2, 3), copies 0..9 behind the ten k-steps of QK,
-  // copies 10..17 behind the first eight PV pairs.  Copies are granule-major,
-  // so tile it + 1 waits for granules 0..3 (copies 0..7) at its top, for
-  // granules 4..7 before it loads k-step 2 and for the RoPE granule before it
-  // loads k-step 4.  The vmcnt values count the copies issued after the
-  // awaited ones.
+  // ids of it + 2 on waves 2, 3), then two copies behind each of the first
+  // nine k-steps of QK, so that every copy has the softmax and the PV of
+  // tile it to land.  Tile it + 1 waits for granules 0..3 (copies 0..7) at
+  // its top, for granules 4..7 (copies 8..15) before it loads k-step 2 and
+  // for the RoPE granule (16, 17) before it loads k-step 4.  The vmcnt
+  // values count the copies issued after the awaited ones.
   // The tile body is instantiated twice: with the next tile's copies
   // (every tile but the last) and without, so that it has no branches on it.
+  // The last tile, when at most 64 of its tokens are valid ("short"),
+  // skips the QK pass over S tiles 4..7 and packs the three P' terms of its
+  // 64 tokens into the k slots of two MFMAs per dim tile instead of three.
   auto tile = [&](auto next_c, int it) {
     constexpr bool next = decltype(next_c)::value;
+    constexpr int NS = 8, NQ = 4, NH = 2;
     wait_vmcnt<10>();
     lds_barrier();                       // granules 0..3 of tile it, its scales, ring(it + 1)
     RowCopies rc{};
     if constexpr (next) {
-      ring_ids(it + 1, id0, id1, idsc);
-      rc = plan_rows(it + 1, id0, id1, idsc);
+      TileIds id;
+      ring_ids(it + 1, id);
+      rc = plan_rows(it + 1, id);
       if (wave < 2) issue_scales(rc, it + 1);
       else issue_ring_slot(min(it + 2, ntiles - 1), (it + 2) % 3);
     }
 
     const DCP_LDS char* sb = smem + (it & 1) * kStageBytes;
     const int tok0 = start + it * kT;
+    const bool short_tile = !next && end - tok0 <= 64;
 
     // ---- S^T = K Q^T (base-2 logits), eight 16-token S tiles in two passes of four
-    f32x4 sacc[8];
+    f32x4 sacc[NS];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 acc[4];
+    for (int half = 0; half < NH; ++half) {
+      if (half == 1 && short_tile) {       // S tiles 4..7 are all masked
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < NQ; ++q) sacc[4 + q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        break;
+      }
+      f32x4 acc[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       auto load_k = [&](int s, i32x8* a) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < NQ; ++q) {
           const int st = 4 * half + q;
           const int cst = ((2 * st) ^ st) & 3;
           if (s < 4) {
@@ -343,50 +394,57 @@ void decode_fp8_kernel(const DecodeParams p) {
       };
       // One operand set: step s + 1 is loaded once step s's MFMAs are
       // issued (they have eight MFMAs of work queued to cover the latency).
-      i32x8 a[4];
+      i32x8 a[NQ];
       load_k(0, a);
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
         // Before k-step s + 1 is loaded: at s = 1 granules 4..7 (copies up to
         // 15; behind them copies 16, 17 of this tile and, with a next tile,
-        // its top copy and copy 0), at s = 3 the RoPE granule (copy 17;
-        // behind it the top copy and copies 0..2 of the next tile).
+        // its top copy and copies 0, 1), at s = 3 the RoPE granule (copy 17;
+        // behind it the top copy and copies 0..5 of the next tile).
         if (half == 0 && s == 1) {
-          if constexpr (next) wait_vmcnt<4>(); else wait_vmcnt<2>();
+          if constexpr (next) wait_vmcnt<5>(); else wait_vmcnt<2>();
           lds_barrier();
         }
         if (half == 0 && s == 3) {
-          if constexpr (next) wait_vmcnt<4>(); else wait_vmcnt<0>();
+          if constexpr (next) wait_vmcnt<7>(); else wait_vmcnt<0>();
           lds_barrier();
         }
         if (s < 4) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < NQ; ++q)
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qhi[s], acc[q], 0, 0,
                                                                      0, 127, 0, qscale);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < NQ; ++q)
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qlo[s], acc[q], 0, 0,
                                                                      0, 127, 0, qscale);
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < NQ; ++q)
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qr, acc[q], 0, 0,
                                                                      0, 127, 0, qscale);
         }
-        if constexpr (next) issue_copy(rc, it + 1, 5 * half + s);
+        if constexpr (next) {
+          const int j = 5 * half + s;
+          if (j < 9) {
+            issue_copy(rc, it + 1, 2 * j);
+            issue_copy(rc, it + 1, 2 * j + 1);
+          }
+        }
         if (s + 1 < 5) load_k(s + 1, a);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sacc[4 * half + q] = acc[q];
+      for (int q = 0; q < NQ; ++q) sacc[4 * half + q] = acc[q];
     }
 
     // First V^T operands, read before the softmax so their latency hides.
-    i32x2 vr[2][2][4];
+    constexpr int NR = 4;                          // tr8 reads per dim tile
+    i32x2 vr[2][2][NR];
     auto load_v = [&](int d, i32x2* r4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < NR; ++r)
         r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (DCP_LDS i32x2*)(sb + (d >> 2) * kGranPlane + 2048 * r + pv_off[(d & 3) ^ (2 * (r & 1))]));
     };
@@ -397,24 +455,24 @@ void decode_fp8_kernel(const DecodeParams p) {
     // reference max only moves when the tile max exceeds it by more than 8
     // (base 2), so O and l are rescaled rarely; p stays <= 2^8.
     // The token scales are read from LDS twice rather than kept in registers.
-    float z[8][4];
+    float z[NS][4];
     float tmax = kNegInf;
     const bool full = tok0 + kT <= end;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+    for (int st = 0; st < NS; ++st) {
       const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[st][i] = sacc[st][i] * s4[i];
     }
     if (!full) {                           // the last tile of the row: mask its tail
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
+      for (int st = 0; st < NS; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (tok0 + 16 * st + 4 * g + i >= end) z[st][i] = kNegInf;
     }
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[st][i]);
     tmax = max_xor32(max_xor16(tmax));
@@ -430,10 +488,10 @@ void decode_fp8_kernel(const DecodeParams p) {
       m_run = m_new;
     }
     const float neg_mc = (m_run == kNegInf) ? 0.f : -m_run * c;
-    float (&pr)[8][4] = z;                 // P' = p * scale replaces the logits
+    float (&pr)[NS][4] = z;                // P' = p * scale replaces the logits
     float pmax = 0.f;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+    for (int st = 0; st < NS; ++st) {
       const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -454,9 +512,9 @@ void decode_fp8_kernel(const DecodeParams p) {
     const int ep = e4m3_exponent(pmax);
     const float ps = pow2i(ep);
     const int pscale = 127 - ep;
-    i32x8 p3[3];
+    i32x8 pb[3];                           // pb[term] byte 4st + i
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+    for (int st = 0; st < NS; ++st) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = pr[st][i] * ps;
@@ -468,41 +526,54 @@ void decode_fp8_kernel(const DecodeParams p) {
       const auto m01 = __builtin_amdgcn_cvt_pk_f32_fp8(m, false);
       const auto m23 = __builtin_amdgcn_cvt_pk_f32_fp8(m, true);
       const int l = pack_e4m3(r0 - m01[0], r1 - m01[1], r2 - m23[0], r3 - m23[1]);
-      p3[0][st] = h;
-      p3[1][st] = m;
-      p3[2][st] = l;
+      pb[0][st] = h;
+      pb[1][st] = m;
+      pb[2][st] = l;
     }
 
-    // ---- O^T += V^T P'^T: 32 dim tiles in 16 pairs, operands one pair ahead
-#pragma unroll
-    for (int grp = 0; grp < 16; ++grp) {
-      if (grp + 1 < 16) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) load_v(2 * (grp + 1) + j, vr[(grp + 1) & 1][j]);
+    // ---- O^T += V^T P'^T: 32 dim tiles in 16 pairs, operands one pair ahead.
+    // k slot byte 4st + i of lane group g is token 16st + 4g + i, one MFMA
+    // per P' term.  A short tile's 64 tokens sit in bytes 0..15 (tr8 reads
+    // 0, 1); its operands repeat them, with the terms (hi, mid) in one MFMA
+    // and (lo, zero) in a second.
+    auto pv = [&](auto short_c) {
+      constexpr bool sh = decltype(short_c)::value;
+      i32x8 pf[2];
+      if constexpr (sh) {
+        pf[0] = i32x8{pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
+        pf[1] = i32x8{pb[2][0], pb[2][1], pb[2][2], pb[2][3], 0, 0, 0, 0};
       }
-      i32x8 vt[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const i32x2* r4 = vr[grp & 1][j];
-        vt[j] = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
+      for (int grp = 0; grp < 16; ++grp) {
+        if (grp + 1 < 16) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) load_v(2 * (grp + 1) + j, vr[(grp + 1) & 1][j]);
+        }
+        i32x8 vt[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const i32x2* r4 = vr[grp & 1][j];
+          vt[j] = sh ? i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[0].x, r4[0].y, r4[1].x, r4[1].y}
+                     : i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
+        }
+        // term-major: two independent accumulators between dependent MFMAs
+#pragma unroll
+        for (int term = 0; term < (sh ? 2 : 3); ++term)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            oacc[2 * grp + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                vt[j], sh ? pf[term] : pb[term], oacc[2 * grp + j], 0, 0, 0, 127, 0, pscale);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (next) {
-        if (grp < 8) issue_copy(rc, it + 1, 10 + grp);
-      }
-      // term-major: two independent accumulators between dependent MFMAs
-#pragma unroll
-      for (int term = 0; term < 3; ++term)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          oacc[2 * grp + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              vt[j], p3[term], oacc[2 * grp + j], 0, 0, 0, 127, 0, pscale);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    if (next || !short_tile) pv(BoolC<false>{});
+    else pv(BoolC<true>{});
   };
-  wait_vmcnt<0>();                       // everything the prologue queued
+  // Tile 0's copies are waited for at its top like any tile's.
   int it = 0;
   for (; it + 1 < ntiles; ++it) tile(BoolC<true>{}, it);
   if (it < ntiles) tile(BoolC<false>{}, it);
+  wait_vmcnt<0>();   // copies queued for tiles that turned out empty
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
   finish_block<kThreads>(p, row, shard, split, head, g, true, oacc, m_run * c, l_tot, smem, &s_flag);

@@ -163,4 +163,10 @@ __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, unsigne
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kCachePolicySc1);
 }
 
+// Plain buffer reads of a bounded table: offsets in bytes, reads past the
+// `bytes` the resource covers return 0 without touching memory.
+__device__ __forceinline__ int load_bounded(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 }  // namespace dcp
