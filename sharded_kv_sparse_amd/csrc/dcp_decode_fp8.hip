@@ -576,7 +576,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   wait_vmcnt<0>();   // copies queued for tiles that turned out empty
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
-  finish_block<kThreads>(p, row, shard, split, head, g, true, oacc, m_run * c, l_tot, smem, &s_flag);
+  finish_block<kThreads, true>(p, row, shard, split, head, g, true, oacc, m_run * c, l_tot, smem, &s_flag);
 }
 
 }  // namespace

@@ -43,6 +43,9 @@ constexpr int kMaxWaitMembers = 24;         // abandon bits 8..31 of the arrival
 // (normalised), and the merged LSE of each head written to out_lse when
 // asked.  Whole block; leaves w in LDS.
 template <int NT>
+__device__ inline void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
+                                              bool write_lse, DCP_LDS float* w);
+template <int NT>
 __device__ inline void merge_weights(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
                                      float* out_lse, bool write_lse, DCP_LDS float* w) {
   const int H = p.heads, tid = threadIdx.x;
@@ -51,6 +54,14 @@ __device__ inline void merge_weights(const DecodeParams& p, long long part0, int
     const int pi = i / nh, hl = i - pi * nh;
     w[pi * kHeadsPerBlock + hl] = load_coherent(rl, (unsigned)(pi * H + h0 + hl) * 4u);
   }
+  merge_weights_from_lds<NT>(n_in, h0, nh, out_lse, write_lse, w);
+}
+
+// The second half of merge_weights: w[i][hl] holds the LSEs.
+template <int NT>
+__device__ inline void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
+                                              bool write_lse, DCP_LDS float* w) {
+  const int tid = threadIdx.x;
   __syncthreads();
   for (int hl = tid; hl < nh; hl += NT) {
     float M = kNegInf;
@@ -130,13 +141,82 @@ __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_
   }
 }
 
+// Merges this block's own part (member `member` of NIN = 4 or 8: dim tiles
+// [d0, d0 + 32 / NIN) of every head of the block, d0 = member * 32 / NIN)
+// with its own normalised values own[j] (dim tile d0 + j) taken from
+// registers instead of the workspace.  Thread (wave w, lane 16g + i16)
+// handles head 16w + i16 and lane group g, the elements it holds.  The other
+// members' values are loaded first and `weights` (which fills w) runs while
+// they are in flight.  Partials are added in index order with the same
+// arithmetic as merge_part, so the result is bit-identical.
+template <int NT, int NIN>
+__device__ inline void merge_own_part(const DecodeParams& p, long long part0, int member, int h0,
+                                      int nh, int hl, int g, const f32x4 (&own)[8],
+                                      DCP_LDS float* w, float* out_lse, bool write_lse, void* out,
+                                      int out_bf16) {
+  constexpr int ND = 32 / NIN;
+  constexpr int NL = (NIN * kHeadsPerBlock + NT - 1) / NT;   // LSE loads per thread
+  const int H = p.heads, tid = threadIdx.x;
+  const int d0 = member * ND;
+  // The LSEs first: vmcnt drains in issue order, so they can be waited for
+  // while the partials are still in flight.
+  const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(p.ws_lse + part0 * H, (unsigned)(NIN * H) * 4u);
+  float lse_in[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int i = tid + k * NT, pi = i / nh, hi = i - pi * nh;
+    lse_in[k] = i < NIN * nh ? load_coherent(rl, (unsigned)(pi * H + h0 + hi) * 4u) : 0.f;
+  }
+  const unsigned part_bytes = (unsigned)H * kVDim * 4u;
+  const __amdgpu_buffer_rsrc_t ro =
+      coherent_rsrc(p.ws_o + part0 * H * kVDim, (unsigned)NIN * part_bytes);
+  const unsigned blk_off = (unsigned)h0 * kVDim * 4u;
+  constexpr unsigned kNowhere = 0x80000000u;      // beyond every resource: reads 0, no traffic
+  f32x4 v[NIN][ND];
+#pragma unroll
+  for (int i = 0; i < NIN; ++i)
+#pragma unroll
+    for (int j = 0; j < ND; ++j)
+      v[i][j] = load_coherent4(
+          ro, i != member ? (unsigned)i * part_bytes + blk_off +
+                                16u * (unsigned)(((d0 + j) * nh + hl) * 4 + g)
+                          : kNowhere);
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int i = tid + k * NT, pi = i / nh, hi = i - pi * nh;
+    if (i < NIN * nh) w[pi * kHeadsPerBlock + hi] = lse_in[k];
+  }
+  merge_weights_from_lds<NT>(NIN, h0, nh, out_lse, write_lse, w);
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NIN; ++i) {
+      const float wt = w[i * kHeadsPerBlock + hl];
+      const f32x4 x = i == member ? own[j] : v[i][j];
+      acc += (wt != 0.f) ? wt * x : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const size_t idx = (size_t)(h0 + hl) * kVDim + 16 * (d0 + j) + 4 * g;
+    if (out_bf16) {
+      const unsigned lo = f32_to_bf16_bits(acc[0]) | ((unsigned)f32_to_bf16_bits(acc[1]) << 16);
+      const unsigned hi = f32_to_bf16_bits(acc[2]) | ((unsigned)f32_to_bf16_bits(acc[3]) << 16);
+      *reinterpret_cast<uint2*>(static_cast<unsigned short*>(out) + idx) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = acc;
+    }
+  }
+}
+
 // Writes this block's normalised partial (O / l and LSE = ln l + max) for
 // its heads to the workspace and/or o_part, then takes part in the merges of
 // its (row, shard, head block) (splits -> o_part) and (row, head block)
 // (everything -> o).  oacc[d][i] holds O^T for dim 16d + 4g + i of `head`;
 // m_run / l_tot are the head's base-2 reference max and its sum of
-// 2^(z - m_run).
-template <int NT>
+// 2^(z - m_run).  OWN: every thread is a writer of its own (head, lane
+// group), heads 16 * wave + lane % 16, so a block that merges its own part
+// in parallel with the others can take its own values from registers and
+// leaves them out of the workspace unless it gives its part up.
+template <int NT, bool OWN = false>
 __device__ inline void finish_block(const DecodeParams& p, long long row, int shard, int split,
                                     int head, int g, bool writer, const f32x4 (&oacc)[32],
                                     float m_run, float l_tot, DCP_LDS char* smem, int* s_flag) {
@@ -152,6 +232,27 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   const long long blk_part = (row * N + shard) * S + split;
+  const int n_in = N * S, member = shard * S + split;
+  const bool may_wait = fused && p.merge_wait_ticks > 0 && n_in <= kMaxWaitMembers;
+  // Own part from registers: dim tiles [od0, od1) of this block's partial are
+  // not stored unless the block gives its part up.
+  const bool own = OWN && may_wait && !need_shard_merge && (n_in == 4 || n_in == 8) && nh * 4 == NT;
+  const int od0 = own ? member * (32 / n_in) : 0, od1 = own ? od0 + 32 / n_in : 0;
+  // The own dim tiles, normalised, in eight registers (a uniform switch, so
+  // that only these stay live through the wait).
+  f32x4 own_v[8];
+  if (own) {
+    switch (od0 >> 2) {
+#define DCP_OWN_CASE(c) \
+      case c: { _Pragma("unroll") for (int j = 0; j < 8; ++j) own_v[j] = oacc[min(4 * c + j, 31)] * inv; } break;
+      DCP_OWN_CASE(0) DCP_OWN_CASE(1) DCP_OWN_CASE(2) DCP_OWN_CASE(3)
+      DCP_OWN_CASE(4) DCP_OWN_CASE(5) DCP_OWN_CASE(6) DCP_OWN_CASE(7)
+#undef DCP_OWN_CASE
+      default: break;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t ws_ro =
+      coherent_rsrc(p.ws_o + (blk_part * H + h0) * kVDim, (unsigned)nh * kVDim * 4u);
   if (writer) {
     if (to_part) {
       float* po = p.o_part + (((long long)shard * p.rows + row) * H + head) * kVDim;
@@ -160,11 +261,10 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
       if (g == 0) p.lse_part[((long long)shard * p.rows + row) * H + head] = lse_v;
     }
     if (to_ws) {
-      const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(p.ws_o + (blk_part * H + h0) * kVDim,
-                                                      (unsigned)nh * kVDim * 4u);
 #pragma unroll
       for (int d = 0; d < 32; ++d)
-        store_coherent4(ro, (unsigned)((d * nh + hl) * 4 + g) * 16u, oacc[d] * inv);
+        if (d < od0 || d >= od1)
+          store_coherent4(ws_ro, (unsigned)((d * nh + hl) * 4 + g) * 16u, oacc[d] * inv);
       if (g == 0) store_coherent(coherent_rsrc(p.ws_lse + blk_part * H, (unsigned)H * 4u),
                                  (unsigned)head * 4u, lse_v);
     }
@@ -195,10 +295,21 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
 
   // ---- all partials of the row -> o.  Arrival word: count in bits 0..7,
   // abandoned parts in bits 8 + member.  Completion word: parts merged.
-  const int n_in = N * S, member = shard * S + split;
   unsigned* arrive = reinterpret_cast<unsigned*>(p.cnt_row + (row * HB + hblk) * 2);
   unsigned* done = arrive + 1;
-  const bool may_wait = p.merge_wait_ticks > 0 && n_in <= kMaxWaitMembers;
+  // Abandons this block's part: with an own part kept in registers, that
+  // part is stored (and waited for) first.  Returns the parts to merge.
+  auto give_up = [&](unsigned now) -> unsigned {
+    for (;;) {
+      if ((now & 0xffu) == (unsigned)n_in) return 1u;
+      unsigned expect = now;
+      if (__hip_atomic_compare_exchange_strong(arrive, &expect, now | (1u << (8 + member)),
+                                               __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        return 0u;                       // abandoned: the last arriver merges this part
+      now = expect;                      // the word moved; look again
+    }
+  };
   if (tid == 0) {
     const unsigned add = 1u + (!may_wait && n_in <= kMaxWaitMembers ? 1u << (8 + member) : 0u);
     const unsigned old = __hip_atomic_fetch_add(arrive, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -212,12 +323,13 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
         const unsigned now = __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((now & 0xffu) == (unsigned)n_in) { parts = 1u; break; }
         if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)p.merge_wait_ticks) {
-          unsigned expect = now;
-          if (__hip_atomic_compare_exchange_strong(arrive, &expect, now | (1u << (8 + member)),
-                                                   __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT))
-            break;                       // abandoned: the last arriver merges this part
-          continue;                      // the word moved; look again
+          if (own) {
+            parts = 4u;                  // timed out: store the own part first
+            s_word[1] = now;
+          } else {
+            parts = give_up(now);
+          }
+          break;
         }
         __builtin_amdgcn_s_sleep(8);
       }
@@ -225,7 +337,20 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
     s_word[0] = parts;
   }
   __syncthreads();
-  const unsigned parts = s_word[0];
+  unsigned parts = s_word[0];
+  if (parts == 4u) {
+    if (writer) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (od0 + j < od1)
+          store_coherent4(ws_ro, (unsigned)(((od0 + j) * nh + hl) * 4 + g) * 16u, own_v[j]);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid == 0) s_word[0] = give_up(s_word[1]);
+    __syncthreads();
+    parts = s_word[0];
+  }
   if (parts == 0u) return;
   // The last arriver merges every part whose member gave up (all parts
   // when there are too many members for abandon bits).
@@ -235,9 +360,20 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
   void* out = p.out_bf16 ? (void*)(static_cast<unsigned short*>(p.o) + row * H * kVDim)
                          : (void*)(static_cast<float*>(p.o) + row * H * kVDim);
   const long long part0 = row * N * S;
-  merge_weights<NT>(p, part0, n_in, h0, nh, p.lse + row * H, (parts & 2u) != 0u, w);
   int merged = 0;
+  if (own && (parts & 1u)) {
+    if (n_in == 4)
+      merge_own_part<NT, 4>(p, part0, member, h0, nh, hl, g, own_v, w, p.lse + row * H,
+                            (parts & 2u) != 0u, out, p.out_bf16);
+    else
+      merge_own_part<NT, 8>(p, part0, member, h0, nh, hl, g, own_v, w, p.lse + row * H,
+                            (parts & 2u) != 0u, out, p.out_bf16);
+    ++merged;
+  } else {
+    merge_weights<NT>(p, part0, n_in, h0, nh, p.lse + row * H, (parts & 2u) != 0u, w);
+  }
   for (int m = 0; m < n_in; ++m) {
+    if (own && m == member) continue;
     if (!(all || m == member || (m < kMaxWaitMembers && ((abandoned >> m) & 1u)))) continue;
     merge_part<NT>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
     ++merged;
