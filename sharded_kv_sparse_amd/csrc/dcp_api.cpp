@@ -82,6 +82,9 @@ WorkspacePlan plan_workspace(long long rows, int heads, int num_shards, int spli
   off = align256(off);
   w.ws_lse_off = off;
   if (w.needs_block_partials) off += sizeof(float) * blocks * heads;
+  off = align256(off);
+  w.ws_exp_off = off;
+  if (w.needs_block_partials) off += sizeof(int) * blocks * heads;
   w.total = (want_merged || (want_partials && splits > 1)) ? align256(off) : 0;
   return w;
 }
@@ -190,6 +193,7 @@ DecodeParams make_params(const CommonArgs& a, const WorkspacePlan& w) {
     p.cnt_shard = reinterpret_cast<int*>(ws + w.cnt_shard_off);
     p.ws_o = reinterpret_cast<float*>(ws + w.ws_o_off);
     p.ws_lse = reinterpret_cast<float*>(ws + w.ws_lse_off);
+    p.ws_exp = reinterpret_cast<int*>(ws + w.ws_exp_off);
   }
   long long blocks = a.rows * a.num_shards * w.splits * p.head_blocks;
   p.xcd_swizzle = (blocks % 8 == 0) ? 1 : 0;

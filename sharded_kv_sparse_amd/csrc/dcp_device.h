@@ -163,6 +163,27 @@ __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, unsigne
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kCachePolicySc1);
 }
 
+// Eight-byte coherent accesses (four fp16 values).
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+__device__ __forceinline__ u32x2 load_coherent2(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ void store_coherent2(__amdgpu_buffer_rsrc_t r, unsigned off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCachePolicySc1);
+}
+// Four floats as fp16 (round to nearest even) and back.  (Whole-vector bit
+// casts only: a bit cast of a single vector element has been seen to lose
+// the other element.)
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 pack_f16x4(f32x4 v) {
+  const f16x4 h = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+  return __builtin_bit_cast(u32x2, h);
+}
+__device__ __forceinline__ f32x4 unpack_f16x4(u32x2 u) {
+  const f16x4 h = __builtin_bit_cast(f16x4, u);
+  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
 // Plain buffer reads of a bounded table: offsets in bytes, reads past the
 // `bytes` the resource covers return 0 without touching memory.
 __device__ __forceinline__ int load_bounded(__amdgpu_buffer_rsrc_t r, unsigned off) {

@@ -41,26 +41,32 @@ constexpr int kMaxWaitMembers = 24;         // abandon bits 8..31 of the arrival
 
 // Weights of the n_in partials of a head block, from their LSEs: w[i][hl]
 // (normalised), and the merged LSE of each head written to out_lse when
-// asked.  Whole block; leaves w in LDS.
+// asked.  With fp16 partials (wx non-null) every weight also carries the
+// partial's power of two 2^wx[i][hl], so that the stored values need no
+// rescaling.  Whole block; leaves w in LDS.
 template <int NT>
 __device__ inline void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
-                                              bool write_lse, DCP_LDS float* w);
+                                              bool write_lse, DCP_LDS float* w, DCP_LDS int* wx);
 template <int NT>
 __device__ inline void merge_weights(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
-                                     float* out_lse, bool write_lse, DCP_LDS float* w) {
+                                     float* out_lse, bool write_lse, DCP_LDS float* w,
+                                     DCP_LDS int* wx) {
   const int H = p.heads, tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(p.ws_lse + part0 * H, (unsigned)(n_in * H) * 4u);
+  const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(p.ws_exp + part0 * H, wx ? (unsigned)(n_in * H) * 4u : 0u);
   for (int i = tid; i < n_in * nh; i += NT) {
     const int pi = i / nh, hl = i - pi * nh;
     w[pi * kHeadsPerBlock + hl] = load_coherent(rl, (unsigned)(pi * H + h0 + hl) * 4u);
+    if (wx) wx[pi * kHeadsPerBlock + hl] = __float_as_int(load_coherent(rx, (unsigned)(pi * H + h0 + hl) * 4u));
   }
-  merge_weights_from_lds<NT>(n_in, h0, nh, out_lse, write_lse, w);
+  merge_weights_from_lds<NT>(n_in, h0, nh, out_lse, write_lse, w, wx);
 }
 
-// The second half of merge_weights: w[i][hl] holds the LSEs.
+// The second half of merge_weights: w[i][hl] holds the LSEs (and wx[i][hl]
+// the powers of two of fp16 partials).
 template <int NT>
 __device__ inline void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
-                                              bool write_lse, DCP_LDS float* w) {
+                                              bool write_lse, DCP_LDS float* w, DCP_LDS int* wx) {
   const int tid = threadIdx.x;
   __syncthreads();
   for (int hl = tid; hl < nh; hl += NT) {
@@ -74,27 +80,46 @@ __device__ inline void merge_weights_from_lds(int n_in, int h0, int nh, float* o
       sum += e;
     }
     const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-    for (int i = 0; i < n_in; ++i) w[i * kHeadsPerBlock + hl] *= inv;
+    for (int i = 0; i < n_in; ++i)
+      w[i * kHeadsPerBlock + hl] *= wx ? inv * pow2i(wx[i * kHeadsPerBlock + hl]) : inv;
     if (write_lse) out_lse[h0 + hl] = sum > 0.f ? M + logf(sum) : kNegInf;
   }
   __syncthreads();
 }
 
+// The workspace partials of a row: fp32, or (HALF) fp16 scaled by a power
+// of two per (partial, head); element e of a head block (dim tile e / 4nh,
+// head (e / 4) % nh, lane group e % 4) holds four consecutive dims.
+template <bool HALF>
+struct WsPartials {
+  static constexpr unsigned kElem = HALF ? 8u : 16u;   // bytes per element
+  __amdgpu_buffer_rsrc_t r;
+  unsigned part_bytes;
+  __device__ WsPartials(const DecodeParams& p, long long part0, int n_in) {
+    part_bytes = (unsigned)p.heads * kVDim * (kElem / 4u);
+    r = coherent_rsrc(reinterpret_cast<const char*>(p.ws_o) + (size_t)part0 * part_bytes,
+                      (unsigned)n_in * part_bytes);
+  }
+  __device__ f32x4 load(unsigned off) const {
+    if constexpr (HALF) return unpack_f16x4(load_coherent2(r, off));
+    else return load_coherent4(r, off);
+  }
+};
+
 // Merges part `part` of `n_parts` of the head block's 128 * nh float4
 // elements (element e: dim tile e / 4nh, head (e / 4) % nh, lane group e % 4)
 // over the partials part0 .. part0 + n_in - 1 into out (the output row's
 // [H][512] values, fp32 or bf16).  Whole block.
-template <int NT>
+template <int NT, bool HALF>
 __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
                                   int part, int n_parts, const DCP_LDS float* w, void* out,
                                   int out_bf16) {
-  const int H = p.heads, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int T = 128 * nh;
   const int e0 = (int)((long long)part * T / n_parts), e1 = (int)((long long)(part + 1) * T / n_parts);
-  const unsigned part_bytes = (unsigned)H * kVDim * 4u;
-  const __amdgpu_buffer_rsrc_t ro =
-      coherent_rsrc(p.ws_o + part0 * H * kVDim, (unsigned)n_in * part_bytes);
-  const unsigned blk_off = (unsigned)h0 * kVDim * 4u;
+  const WsPartials<HALF> ws(p, part0, n_in);
+  const unsigned part_bytes = ws.part_bytes;
+  const unsigned blk_off = (unsigned)h0 * 128u * ws.kElem;
   constexpr unsigned kNowhere = 0x80000000u;      // beyond every resource: reads 0, no traffic
   constexpr int K = 8;                             // elements per thread per pass
   for (int eb = e0; eb < e1; eb += NT * K) {
@@ -114,7 +139,7 @@ __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_
         for (int k = 0; k < K; ++k) {
           const int e = eb + k * NT + tid;
           const bool live = i0 + u < n_in && e < e1;
-          v[u][k] = load_coherent4(ro, live ? (unsigned)(i0 + u) * part_bytes + blk_off + 16u * e : kNowhere);
+          v[u][k] = ws.load(live ? (unsigned)(i0 + u) * part_bytes + blk_off + ws.kElem * e : kNowhere);
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -149,11 +174,11 @@ __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_
 // members' values are loaded first and `weights` (which fills w) runs while
 // they are in flight.  Partials are added in index order with the same
 // arithmetic as merge_part, so the result is bit-identical.
-template <int NT, int NIN>
+template <int NT, int NIN, bool HALF>
 __device__ inline void merge_own_part(const DecodeParams& p, long long part0, int member, int h0,
                                       int nh, int hl, int g, const f32x4 (&own)[8],
-                                      DCP_LDS float* w, float* out_lse, bool write_lse, void* out,
-                                      int out_bf16) {
+                                      DCP_LDS float* w, DCP_LDS int* wx, float* out_lse,
+                                      bool write_lse, void* out, int out_bf16) {
   constexpr int ND = 32 / NIN;
   constexpr int NL = (NIN * kHeadsPerBlock + NT - 1) / NT;   // LSE loads per thread
   const int H = p.heads, tid = threadIdx.x;
@@ -161,32 +186,37 @@ __device__ inline void merge_own_part(const DecodeParams& p, long long part0, in
   // The LSEs first: vmcnt drains in issue order, so they can be waited for
   // while the partials are still in flight.
   const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(p.ws_lse + part0 * H, (unsigned)(NIN * H) * 4u);
+  const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(p.ws_exp + part0 * H, HALF ? (unsigned)(NIN * H) * 4u : 0u);
   float lse_in[NL];
+  int exp_in[NL];
 #pragma unroll
   for (int k = 0; k < NL; ++k) {
     const int i = tid + k * NT, pi = i / nh, hi = i - pi * nh;
-    lse_in[k] = i < NIN * nh ? load_coherent(rl, (unsigned)(pi * H + h0 + hi) * 4u) : 0.f;
+    const unsigned off = (unsigned)(pi * H + h0 + hi) * 4u;
+    lse_in[k] = i < NIN * nh ? load_coherent(rl, off) : 0.f;
+    exp_in[k] = HALF && i < NIN * nh ? __float_as_int(load_coherent(rx, off)) : 0;
   }
-  const unsigned part_bytes = (unsigned)H * kVDim * 4u;
-  const __amdgpu_buffer_rsrc_t ro =
-      coherent_rsrc(p.ws_o + part0 * H * kVDim, (unsigned)NIN * part_bytes);
-  const unsigned blk_off = (unsigned)h0 * kVDim * 4u;
+  const WsPartials<HALF> ws(p, part0, NIN);
+  const unsigned part_bytes = ws.part_bytes;
+  const unsigned blk_off = (unsigned)h0 * 128u * ws.kElem;
   constexpr unsigned kNowhere = 0x80000000u;      // beyond every resource: reads 0, no traffic
   f32x4 v[NIN][ND];
 #pragma unroll
   for (int i = 0; i < NIN; ++i)
 #pragma unroll
     for (int j = 0; j < ND; ++j)
-      v[i][j] = load_coherent4(
-          ro, i != member ? (unsigned)i * part_bytes + blk_off +
-                                16u * (unsigned)(((d0 + j) * nh + hl) * 4 + g)
-                          : kNowhere);
+      v[i][j] = ws.load(i != member ? (unsigned)i * part_bytes + blk_off +
+                                          ws.kElem * (unsigned)(((d0 + j) * nh + hl) * 4 + g)
+                                    : kNowhere);
 #pragma unroll
   for (int k = 0; k < NL; ++k) {
     const int i = tid + k * NT, pi = i / nh, hi = i - pi * nh;
-    if (i < NIN * nh) w[pi * kHeadsPerBlock + hi] = lse_in[k];
+    if (i < NIN * nh) {
+      w[pi * kHeadsPerBlock + hi] = lse_in[k];
+      if (HALF) wx[pi * kHeadsPerBlock + hi] = exp_in[k];
+    }
   }
-  merge_weights_from_lds<NT>(NIN, h0, nh, out_lse, write_lse, w);
+  merge_weights_from_lds<NT>(NIN, h0, nh, out_lse, write_lse, w, HALF ? wx : nullptr);
 #pragma unroll
   for (int j = 0; j < ND; ++j) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -236,23 +266,52 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
   const bool may_wait = fused && p.merge_wait_ticks > 0 && n_in <= kMaxWaitMembers;
   // Own part from registers: dim tiles [od0, od1) of this block's partial are
   // not stored unless the block gives its part up.
-  const bool own = OWN && may_wait && !need_shard_merge && (n_in == 4 || n_in == 8) && nh * 4 == NT;
+  const bool own = OWN && may_wait && !need_shard_merge && n_in == 4 && nh * 4 == NT;
   const int od0 = own ? member * (32 / n_in) : 0, od1 = own ? od0 + 32 / n_in : 0;
-  // The own dim tiles, normalised, in eight registers (a uniform switch, so
+  // The row merge exchanges fp16 partials (the merge of one shard's splits
+  // into o_part keeps fp32): each (partial, head) is scaled by a power of
+  // two 2^-ex that puts its largest magnitude in [2^14, 2^15), so every value
+  // keeps 11 significant bits (the merge weights carry the 2^ex back).
+  const bool half_ws = fused && !need_shard_merge;
+  int ex = 0;
+  float sc = 1.f;
+  if (half_ws && writer) {
+    float amax = 0.f;
+#pragma unroll
+    for (int d = 0; d < 32; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(oacc[d][i]));
+    amax = max_xor32(max_xor16(amax * inv));
+    const int F = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+    ex = amax > 0.f ? min(max(F - 141, -100), 100) : 0;
+    sc = pow2i(-ex);
+  }
+  // A dim tile's workspace value: fp32 O / l, or its fp16 image back in fp32.
+  auto ws_value = [&](const f32x4& o) -> f32x4 {
+    return half_ws ? unpack_f16x4(pack_f16x4(o * inv * sc)) : o * inv;
+  };
+  // The own dim tiles, as stored, in eight registers (a uniform switch, so
   // that only these stay live through the wait).
   f32x4 own_v[8];
   if (own) {
     switch (od0 >> 2) {
 #define DCP_OWN_CASE(c) \
-      case c: { _Pragma("unroll") for (int j = 0; j < 8; ++j) own_v[j] = oacc[min(4 * c + j, 31)] * inv; } break;
+      case c: { _Pragma("unroll") for (int j = 0; j < 8; ++j) own_v[j] = ws_value(oacc[min(4 * c + j, 31)]); } break;
       DCP_OWN_CASE(0) DCP_OWN_CASE(1) DCP_OWN_CASE(2) DCP_OWN_CASE(3)
       DCP_OWN_CASE(4) DCP_OWN_CASE(5) DCP_OWN_CASE(6) DCP_OWN_CASE(7)
 #undef DCP_OWN_CASE
       default: break;
     }
   }
+  const unsigned ws_elem = half_ws ? 8u : 16u;    // workspace bytes per 4 dims
   const __amdgpu_buffer_rsrc_t ws_ro =
-      coherent_rsrc(p.ws_o + (blk_part * H + h0) * kVDim, (unsigned)nh * kVDim * 4u);
+      coherent_rsrc(reinterpret_cast<const char*>(p.ws_o) + (size_t)(blk_part * H + h0) * 128u * ws_elem,
+                    (unsigned)nh * 128u * ws_elem);
+  auto store_ws = [&](int d, const f32x4& o) {
+    const unsigned off = (unsigned)((d * nh + hl) * 4 + g) * ws_elem;
+    if (half_ws) store_coherent2(ws_ro, off, pack_f16x4(o * inv * sc));
+    else store_coherent4(ws_ro, off, o * inv);
+  };
   if (writer) {
     if (to_part) {
       float* po = p.o_part + (((long long)shard * p.rows + row) * H + head) * kVDim;
@@ -263,10 +322,14 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
     if (to_ws) {
 #pragma unroll
       for (int d = 0; d < 32; ++d)
-        if (d < od0 || d >= od1)
-          store_coherent4(ws_ro, (unsigned)((d * nh + hl) * 4 + g) * 16u, oacc[d] * inv);
-      if (g == 0) store_coherent(coherent_rsrc(p.ws_lse + blk_part * H, (unsigned)H * 4u),
-                                 (unsigned)head * 4u, lse_v);
+        if (d < od0 || d >= od1) store_ws(d, oacc[d]);
+      if (g == 0) {
+        store_coherent(coherent_rsrc(p.ws_lse + blk_part * H, (unsigned)H * 4u),
+                       (unsigned)head * 4u, lse_v);
+        if (half_ws)
+          store_coherent(coherent_rsrc(p.ws_exp + blk_part * H, (unsigned)H * 4u),
+                         (unsigned)head * 4u, __int_as_float(ex));
+      }
     }
   }
   if (!to_ws) return;
@@ -275,6 +338,7 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
   __syncthreads();       // ... and so have those of every thread of the block
   DCP_LDS float* w = (DCP_LDS float*)smem;                    // [kMaxMergeInputs][64]
   DCP_LDS unsigned* s_word = (DCP_LDS unsigned*)(w + kMaxMergeInputs * kHeadsPerBlock);
+  DCP_LDS int* wx = (DCP_LDS int*)(s_word + 64);              // [kMaxMergeInputs][64]
 
   if (need_shard_merge) {
     // splits of one shard -> o_part: the last of the S blocks merges
@@ -284,8 +348,9 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
     __syncthreads();
     if (*s_flag) {
       const long long part0 = (row * N + shard) * S;
-      merge_weights<NT>(p, part0, S, h0, nh, p.lse_part + ((long long)shard * p.rows + row) * H, true, w);
-      merge_part<NT>(p, part0, S, h0, nh, 0, 1, w,
+      merge_weights<NT>(p, part0, S, h0, nh, p.lse_part + ((long long)shard * p.rows + row) * H, true, w,
+                        nullptr);
+      merge_part<NT, false>(p, part0, S, h0, nh, 0, 1, w,
                      p.o_part + ((long long)shard * p.rows + row) * H * kVDim, 0);
       if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -341,9 +406,9 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
   if (parts == 4u) {
     if (writer) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 8; ++j)    // own_v holds the fp16 image: re-packing is exact
         if (od0 + j < od1)
-          store_coherent4(ws_ro, (unsigned)(((od0 + j) * nh + hl) * 4 + g) * 16u, own_v[j]);
+          store_coherent2(ws_ro, (unsigned)(((od0 + j) * nh + hl) * 4 + g) * 8u, pack_f16x4(own_v[j]));
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -361,21 +426,20 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
                          : (void*)(static_cast<float*>(p.o) + row * H * kVDim);
   const long long part0 = row * N * S;
   int merged = 0;
-  if (own && (parts & 1u)) {
-    if (n_in == 4)
-      merge_own_part<NT, 4>(p, part0, member, h0, nh, hl, g, own_v, w, p.lse + row * H,
-                            (parts & 2u) != 0u, out, p.out_bf16);
-    else
-      merge_own_part<NT, 8>(p, part0, member, h0, nh, hl, g, own_v, w, p.lse + row * H,
-                            (parts & 2u) != 0u, out, p.out_bf16);
+  float* out_lse = p.lse + row * H;
+  const bool last = (parts & 2u) != 0u;
+  if (own && (parts & 1u)) {       // (own implies the fp16 workspace)
+    merge_own_part<NT, 4, true>(p, part0, member, h0, nh, hl, g, own_v, w, wx, out_lse, last, out,
+                                p.out_bf16);
     ++merged;
   } else {
-    merge_weights<NT>(p, part0, n_in, h0, nh, p.lse + row * H, (parts & 2u) != 0u, w);
+    merge_weights<NT>(p, part0, n_in, h0, nh, out_lse, last, w, half_ws ? wx : nullptr);
   }
   for (int m = 0; m < n_in; ++m) {
     if (own && m == member) continue;
     if (!(all || m == member || (m < kMaxWaitMembers && ((abandoned >> m) & 1u)))) continue;
-    merge_part<NT>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
+    if (half_ws) merge_part<NT, true>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
+    else merge_part<NT, false>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
     ++merged;
   }
   __syncthreads();

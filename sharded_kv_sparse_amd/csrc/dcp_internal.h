@@ -51,6 +51,7 @@ struct DecodeParams {
   // workspace
   float* ws_o;                   // [rows, N, S, heads, 512]
   float* ws_lse;                 // [rows, N, S, heads]
+  int* ws_exp;                   // [rows, N, S, heads]: power of two of an fp16 row-merge partial
   int* cnt_row;                  // [rows, head blocks, 2]: arrival and completion words
   int* cnt_shard;                // [rows, N, head blocks]
   int xcd_swizzle;               // grid is a multiple of 8: keep a row's blocks on one XCD
@@ -63,7 +64,7 @@ struct WorkspacePlan {
   bool fused;
   bool partials;
   bool needs_block_partials;     // blocks write split partials to the workspace
-  size_t cnt_row_off, cnt_shard_off, ws_o_off, ws_lse_off, total;
+  size_t cnt_row_off, cnt_shard_off, ws_o_off, ws_lse_off, ws_exp_off, total;
 };
 
 int default_splits(long long rows, int num_shards, long long tokens_per_shard_expected,

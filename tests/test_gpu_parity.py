@@ -210,7 +210,12 @@ def test_fused_equals_unfused_and_counters_reset(gpu):
     assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
     hb = (p.heads + 63) // 64
     assert (ws[: 8 * p.rows * hb].view(torch.int32) == 0).all()    # arrival + completion words
-    np.testing.assert_allclose(to_np(a["o"]), to_np(o_c), rtol=0, atol=1e-5)
+    # The fused merge exchanges the partials as fp16 with a power of two per
+    # (partial, head) that puts the head's largest magnitude in [2^14, 2^15):
+    # every value is off by at most 2^-11 of its head's largest partial value
+    # (the merge weights sum to 1); the LSEs are exchanged in fp32.
+    bound = 2.0 ** -11 * float(parts["o_part"].abs().max()) + 1e-5
+    np.testing.assert_allclose(to_np(a["o"]), to_np(o_c), rtol=0, atol=bound)
     np.testing.assert_allclose(to_np(a["lse"]), to_np(lse_c), rtol=0, atol=1e-5)
     check_against_oracle(a, oracle_sparse(w), "fused")
 
