@@ -189,36 +189,29 @@ void decode_fp8_kernel(const DecodeParams p) {
   ids0.sc = id_at(start + tok_cap(sc_tok));
   const int id_first = id_at(start);
 
-  // ---- query loads.  Latent k-step s < 4: lane group g holds dims 128s +
-  // 32g .. +32; RoPE: dims 512 + 16g .. +16.
-  const int head = hblk * kHeadsPerBlock + wave * 16 + i16;
-  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + head) * kHeadDim;
-  bf16x8 raw[4][4], raw_r[2];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      raw[s][u] = *reinterpret_cast<const bf16x8*>(qrow + 128 * s + 32 * g + 8 * u);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) raw_r[u] = *reinterpret_cast<const bf16x8*>(qrow + 512 + 16 * g + 8 * u);
-  // The query and the ids are waited for here, before any copy is queued: the waits the
-  // compiler places before the first use of a load do not count the copies
-  // (inline global->LDS instructions), so a use after them would also wait
-  // for every copy of tile 0.
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) touch(raw[s][u]);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) touch(raw_r[u]);
   touch(ids0.id[0]);
   touch(ids0.id[1]);
   touch(ids0.sc);
   touch(id_first);
 
+  // ---- the query of the wave's 16 heads (18 KB, contiguous) is copied into
+  // stage 1, idle until tile 1's copies, by the same global->LDS DMA as the
+  // keys, so that it streams in together with tile 0.  (Register loads would
+  // have to land before the first copy is queued: the waits the compiler
+  // places before a load's first use do not count the inline copies, so a
+  // use after them would also wait for every copy of tile 0.)
+  const int head = hblk * kHeadsPerBlock + wave * 16 + i16;
+  constexpr int kQWaveBytes = 16 * kHeadDim * 2;
+  DCP_LDS char* q_lds = smem + kStageBytes + wave * kQWaveBytes;
+  {
+    const char* qw = static_cast<const char*>(p.q) +
+                     ((size_t)row * H + hblk * kHeadsPerBlock + wave * 16) * kHeadDim * 2;
+#pragma unroll
+    for (int i = 0; i < kQWaveBytes / 1024; ++i) dma16(qw + 1024 * i + 16 * lane, q_lds + 1024 * i);
+  }
+
   // ---- tile 0: the scales (waves 0, 1) or the ids of tile 1 (waves 2, 3)
-  // first, as at the top of every tile, then granules 0..3 (copies 0..7);
-  // the rest follows the query split below.
+  // first, as at the top of every tile, then all its copies.
   const bool issue0 = ntiles > 0, ring1 = ntiles > 1;
   {
     auto valid0 = [&](int t) { return start + t < end; };
@@ -231,9 +224,26 @@ void decode_fp8_kernel(const DecodeParams p) {
   if (wave >= 2 && ring1) issue_ring_slot(1, 1);
   if (issue0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) issue_copy(rc0, 0, c);
+    for (int c = 0; c < 18; ++c) issue_copy(rc0, 0, c);
+    wait_vmcnt<18>();                  // the query (tile 0's 18 copies stay in flight)
+  } else {
+    wait_vmcnt<0>();
   }
-  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- query from LDS.  Latent k-step s < 4: lane group g holds dims 128s +
+  // 32g .. +32; RoPE: dims 512 + 16g .. +16.
+  bf16x8 raw[4][4], raw_r[2];
+  {
+    const DCP_LDS char* qh = q_lds + i16 * (kHeadDim * 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        raw[s][u] = *reinterpret_cast<const DCP_LDS bf16x8*>(qh + 2 * (128 * s + 32 * g + 8 * u));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      raw_r[u] = *reinterpret_cast<const DCP_LDS bf16x8*>(qh + 2 * (512 + 16 * g + 8 * u));
+  }
 
   // ---- query: Q * 2^e as E4M3 hi + lo (e per head: the largest with
   // max |Q| * 2^e <= 448; a bf16 value has 8 significant bits, so hi + lo is
@@ -290,11 +300,6 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) asm volatile("" : "+a"(qhi[s]), "+a"(qlo[s]));
     asm volatile("" : "+a"(qr));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if (issue0) {
-#pragma unroll
-    for (int c = 8; c < 18; ++c) issue_copy(rc0, 0, c);
   }
 
   // ---- online-softmax state; lane: head column, O^T dims 16d + 4g + i.
