@@ -341,12 +341,14 @@ void decode_fp8_kernel(const DecodeParams p) {
 
   // Copy schedule of tile it + 1 while tile it is computed (per wave, in
   // this order): one 4-byte copy at the top (scales of it + 1 on waves 0, 1;
-  // ids of it + 2 on waves 2, 3), then two copies behind each of the first
-  // nine k-steps of QK, so that every copy has the softmax and the PV of
-  // tile it to land.  Tile it + 1 waits for granules 0..3 (copies 0..7) at
-  // its top, for granules 4..7 (copies 8..15) before it loads k-step 2 and
-  // for the RoPE granule (16, 17) before it loads k-step 4.  The vmcnt
-  // values count the copies issued after the awaited ones.
+  // ids of it + 2 on waves 2, 3), copies 0..8 behind the first nine k-steps
+  // of QK, 9..13 spread over the softmax and 14..17 behind the first four PV
+  // pairs: about one copy per 400 cycles, the rate at which a CU's share of
+  // the memory system drains them when every CU is copying, so the wave
+  // rarely stalls at an issue.  Tile it + 1 waits for granules 0..3 (copies
+  // 0..7) at its top, for granules 4..7 (copies 8..15) before it loads
+  // k-step 2 and for the RoPE granule (16, 17) before it loads k-step 4.  The
+  // vmcnt values count the copies issued after the awaited ones.
   // The tile body is instantiated twice: with the next tile's copies
   // (every tile but the last) and without, so that it has no branches on it.
   // The last tile, when at most 64 of its tokens are valid ("short"),
@@ -366,6 +368,14 @@ void decode_fp8_kernel(const DecodeParams p) {
       else issue_ring_slot(min(it + 2, ntiles - 1), (it + 2) % 3);
     }
 
+    // Copy c of the next tile at this point of the instruction stream.
+    auto copy_at = [&](int c) {
+      if constexpr (next) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_copy(rc, it + 1, c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
     const DCP_LDS char* sb = smem + (it & 1) * kStageBytes;
     const int tok0 = start + it * kT;
     const bool short_tile = !next && end - tok0 <= 64;
@@ -405,14 +415,14 @@ void decode_fp8_kernel(const DecodeParams p) {
       for (int s = 0; s < 5; ++s) {
         // Before k-step s + 1 is loaded: at s = 1 granules 4..7 (copies up to
         // 15; behind them copies 16, 17 of this tile and, with a next tile,
-        // its top copy and copies 0, 1), at s = 3 the RoPE granule (copy 17;
-        // behind it the top copy and copies 0..5 of the next tile).
+        // its top copy and copy 0), at s = 3 the RoPE granule (copy 17;
+        // behind it the top copy and copies 0..2 of the next tile).
         if (half == 0 && s == 1) {
-          if constexpr (next) wait_vmcnt<5>(); else wait_vmcnt<2>();
+          if constexpr (next) wait_vmcnt<4>(); else wait_vmcnt<2>();
           lds_barrier();
         }
         if (half == 0 && s == 3) {
-          if constexpr (next) wait_vmcnt<7>(); else wait_vmcnt<0>();
+          if constexpr (next) wait_vmcnt<4>(); else wait_vmcnt<0>();
           lds_barrier();
         }
         if (s < 4) {
@@ -432,10 +442,7 @@ void decode_fp8_kernel(const DecodeParams p) {
         }
         if constexpr (next) {
           const int j = 5 * half + s;
-          if (j < 9) {
-            issue_copy(rc, it + 1, 2 * j);
-            issue_copy(rc, it + 1, 2 * j + 1);
-          }
+          if (j < 9) issue_copy(rc, it + 1, j);
         }
         if (s + 1 < 5) load_k(s + 1, a);
         __builtin_amdgcn_sched_barrier(0);
@@ -469,6 +476,7 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[st][i] = sacc[st][i] * s4[i];
     }
+    copy_at(9);
     if (!full) {                           // the last tile of the row: mask its tail
 #pragma unroll
       for (int st = 0; st < NS; ++st)
@@ -481,6 +489,7 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[st][i]);
     tmax = max_xor32(max_xor16(tmax));
+    copy_at(10);
     const bool bump = tmax > m_run + bump_gap;
     if (__any(bump)) {
       const float m_new = bump ? tmax : m_run;
@@ -506,6 +515,7 @@ void decode_fp8_kernel(const DecodeParams p) {
         pmax = fmaxf(pmax, pr[st][i]);
       }
     }
+    copy_at(11);
 
     // ---- P' of the head's 128 tokens as three E4M3 terms at one power of two
     // per head; the MFMA's B block scale (127 - ep) multiplies it back out.
@@ -534,6 +544,8 @@ void decode_fp8_kernel(const DecodeParams p) {
       pb[0][st] = h;
       pb[1][st] = m;
       pb[2][st] = l;
+      if (st == 2) copy_at(12);
+      if (st == 5) copy_at(13);
     }
 
     // ---- O^T += V^T P'^T: 32 dim tiles in 16 pairs, operands one pair ahead.
@@ -560,6 +572,9 @@ void decode_fp8_kernel(const DecodeParams p) {
           const i32x2* r4 = vr[grp & 1][j];
           vt[j] = sh ? i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[0].x, r4[0].y, r4[1].x, r4[1].y}
                      : i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
+        }
+        if constexpr (next) {
+          if (grp < 4) issue_copy(rc, it + 1, 14 + grp);
         }
         // term-major: two independent accumulators between dependent MFMAs
 #pragma unroll
