@@ -308,6 +308,12 @@ void decode_fp8_kernel(const DecodeParams p) {
   const float bump_gap = 8.0f / c;   // the reference moves when a tile beats it by 2^8
   float m_run = kNegInf;    // reference max of y, moves lazily
   float l_run = 0.f;        // this lane's share of sum 2^(c (y - m_run))
+  float smax = 0.f;         // largest |token scale| this lane has read
+  // Set by the last tile: the block's l, the fp16 exponent of its workspace
+  // partial and whether that partial was stored during the last PV.
+  float l_fin = 0.f;
+  int ex_ws = kExFromValues;
+  bool pre_stored = false;
   f32x4 oacc[32];
 #pragma unroll
   for (int d = 0; d < 32; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -511,6 +517,7 @@ void decode_fp8_kernel(const DecodeParams p) {
       for (int i = 0; i < 4; ++i) {
         const float e = fast_exp2(fmaf(z[st][i], c, neg_mc));
         l_run += e;
+        smax = fmaxf(smax, fabsf(s4[i]));
         pr[st][i] = e * s4[i];
         pmax = fmaxf(pmax, pr[st][i]);
       }
@@ -548,6 +555,26 @@ void decode_fp8_kernel(const DecodeParams p) {
       if (st == 5) copy_at(13);
     }
 
+    // ---- The last tile stores the workspace partial during its PV, each
+    // dim-tile pair right behind its final MFMAs.  l is complete once the
+    // softmax has run, and |O / l| <= 448 * (largest token scale), since O / l
+    // is a convex combination of scaled E4M3 values: that bound fixes the
+    // fp16 exponent before O is known.
+    const bool ws_early = !next && (p.o != nullptr || (p.o_part != nullptr && p.num_splits > 1));
+    if constexpr (!next) {
+      l_fin = sum_xor32(sum_xor16(l_run));
+      ex_ws = half_exponent(448.0f * max_xor32(max_xor16(smax)));
+      pre_stored = ws_early;
+    }
+    const WsPartial<kThreads, true> wsp(p, row, shard, split, head, g,
+                                         l_fin > 0.f ? 1.0f / l_fin : 0.f, ex_ws);
+    auto store_pair = [&](int pair) {
+      if (ws_early && !wsp.is_own(2 * pair)) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wsp.store(2 * pair + j, oacc[2 * pair + j]);
+      }
+    };
+
     // ---- O^T += V^T P'^T: 32 dim tiles in 16 pairs, operands one pair ahead.
     // k slot byte 4st + i of lane group g is token 16st + 4g + i, one MFMA
     // per P' term.  A short tile's 64 tokens sit in bytes 0..15 (tr8 reads
@@ -583,8 +610,12 @@ void decode_fp8_kernel(const DecodeParams p) {
           for (int j = 0; j < 2; ++j)
             oacc[2 * grp + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 vt[j], sh ? pf[term] : pb[term], oacc[2 * grp + j], 0, 0, 0, 127, 0, pscale);
+        if constexpr (!next) {
+          if (grp > 0) store_pair(grp - 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (!next) store_pair(15);
     };
     if (next || !short_tile) pv(BoolC<false>{});
     else pv(BoolC<true>{});
@@ -596,7 +627,8 @@ void decode_fp8_kernel(const DecodeParams p) {
   wait_vmcnt<0>();   // copies queued for tiles that turned out empty
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
-  finish_block<kThreads, true>(p, row, shard, split, head, g, true, oacc, m_run * c, l_tot, smem, &s_flag);
+  finish_block<kThreads, true>(p, row, shard, split, head, g, true, oacc, m_run * c, l_tot, smem, &s_flag,
+                               ex_ws, pre_stored);
 }
 
 }  // namespace

@@ -237,6 +237,60 @@ __device__ inline void merge_own_part(const DecodeParams& p, long long part0, in
   }
 }
 
+// Power of two of a block's fp16 row-merge partial: ex with every |value| *
+// 2^-ex below 2^15, from a bound on the values (their largest magnitude, or
+// any larger bound): the bound lands in [2^14, 2^15).
+__device__ __forceinline__ int half_exponent(float bound) {
+  const int F = (int)((__float_as_uint(bound) >> 23) & 0xffu);
+  return bound > 0.f ? min(max(F - 141, -100), 100) : 0;
+}
+constexpr int kExFromValues = -1000;         // finish_block: exponent from the values
+
+// Where and how a block's workspace partial is stored: fp16 scaled by
+// 2^-ex for the row merge, fp32 for the merge of one shard's splits; the
+// own dim tiles [od0, od1) of a block that merges its own part in parallel
+// stay in registers.  Element (d, head, lane group g) holds dims 16d + 4g..
+template <int NT, bool OWN>
+struct WsPartial {
+  bool half;
+  int od0, od1, nh, hl, g, ex;
+  float scale;                               // O -> stored value
+  unsigned elem;                             // bytes per element
+  __amdgpu_buffer_rsrc_t r;
+  __device__ WsPartial(const DecodeParams& p, long long row, int shard, int split, int head,
+                       int g_, float inv, int ex_) {
+    const int N = p.num_shards, S = p.num_splits, H = p.heads;
+    const int h0 = head / kHeadsPerBlock * kHeadsPerBlock;
+    nh = min(kHeadsPerBlock, H - h0);
+    hl = head - h0;
+    g = g_;
+    const bool need_shard_merge = p.o_part != nullptr && S > 1;
+    const bool fused = p.o != nullptr;
+    const int n_in = N * S, member = shard * S + split;
+    const bool may_wait = fused && p.merge_wait_ticks > 0 && n_in <= kMaxWaitMembers;
+    const bool own = OWN && may_wait && !need_shard_merge && n_in == 4 && nh * 4 == NT;
+    od0 = own ? member * (32 / n_in) : 0;
+    od1 = own ? od0 + 32 / n_in : 0;
+    half = fused && !need_shard_merge;
+    ex = half ? ex_ : 0;
+    scale = half ? inv * pow2i(-ex) : inv;
+    elem = half ? 8u : 16u;
+    const long long blk_part = (row * N + shard) * S + split;
+    r = coherent_rsrc(reinterpret_cast<const char*>(p.ws_o) + (size_t)(blk_part * H + h0) * 128u * elem,
+                      (unsigned)nh * 128u * elem);
+  }
+  __device__ bool is_own(int d) const { return d >= od0 && d < od1; }
+  // The value as the merge sees it (fp16 image back in fp32).
+  __device__ f32x4 value(const f32x4& o) const {
+    return half ? unpack_f16x4(pack_f16x4(o * scale)) : o * scale;
+  }
+  __device__ void store(int d, const f32x4& o) const {
+    const unsigned off = (unsigned)((d * nh + hl) * 4 + g) * elem;
+    if (half) store_coherent2(r, off, pack_f16x4(o * scale));
+    else store_coherent4(r, off, o * scale);
+  }
+};
+
 // Writes this block's normalised partial (O / l and LSE = ln l + max) for
 // its heads to the workspace and/or o_part, then takes part in the merges of
 // its (row, shard, head block) (splits -> o_part) and (row, head block)
@@ -246,10 +300,14 @@ __device__ inline void merge_own_part(const DecodeParams& p, long long part0, in
 // group), heads 16 * wave + lane % 16, so a block that merges its own part
 // in parallel with the others can take its own values from registers and
 // leaves them out of the workspace unless it gives its part up.
+// ex_given: the fp16 exponent when the caller has a bound (else it comes
+// from the values); pre_stored: the caller already stored the non-own dim
+// tiles of its workspace partial (with that exponent).
 template <int NT, bool OWN = false>
 __device__ inline void finish_block(const DecodeParams& p, long long row, int shard, int split,
                                     int head, int g, bool writer, const f32x4 (&oacc)[32],
-                                    float m_run, float l_tot, DCP_LDS char* smem, int* s_flag) {
+                                    float m_run, float l_tot, DCP_LDS char* smem, int* s_flag,
+                                    int ex_given = kExFromValues, bool pre_stored = false) {
   const int tid = threadIdx.x;
   const int N = p.num_shards, S = p.num_splits, HB = p.head_blocks, H = p.heads;
   const int hblk = head / kHeadsPerBlock;
@@ -264,54 +322,42 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
   const long long blk_part = (row * N + shard) * S + split;
   const int n_in = N * S, member = shard * S + split;
   const bool may_wait = fused && p.merge_wait_ticks > 0 && n_in <= kMaxWaitMembers;
-  // Own part from registers: dim tiles [od0, od1) of this block's partial are
-  // not stored unless the block gives its part up.
-  const bool own = OWN && may_wait && !need_shard_merge && n_in == 4 && nh * 4 == NT;
-  const int od0 = own ? member * (32 / n_in) : 0, od1 = own ? od0 + 32 / n_in : 0;
   // The row merge exchanges fp16 partials (the merge of one shard's splits
   // into o_part keeps fp32): each (partial, head) is scaled by a power of
-  // two 2^-ex that puts its largest magnitude in [2^14, 2^15), so every value
-  // keeps 11 significant bits (the merge weights carry the 2^ex back).
+  // two 2^-ex that keeps every |value| below 2^15, so every value keeps 11
+  // significant bits (the merge weights carry the 2^ex back).
   const bool half_ws = fused && !need_shard_merge;
   int ex = 0;
-  float sc = 1.f;
   if (half_ws && writer) {
-    float amax = 0.f;
+    if (ex_given != kExFromValues) {
+      ex = ex_given;
+    } else {
+      float amax = 0.f;
 #pragma unroll
-    for (int d = 0; d < 32; ++d)
+      for (int d = 0; d < 32; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(oacc[d][i]));
-    amax = max_xor32(max_xor16(amax * inv));
-    const int F = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-    ex = amax > 0.f ? min(max(F - 141, -100), 100) : 0;
-    sc = pow2i(-ex);
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(oacc[d][i]));
+      ex = half_exponent(max_xor32(max_xor16(amax * inv)));
+    }
   }
-  // A dim tile's workspace value: fp32 O / l, or its fp16 image back in fp32.
-  auto ws_value = [&](const f32x4& o) -> f32x4 {
-    return half_ws ? unpack_f16x4(pack_f16x4(o * inv * sc)) : o * inv;
-  };
+  const WsPartial<NT, OWN> wsp(p, row, shard, split, head, g, inv, ex);
+  // Own part from registers: dim tiles [od0, od1) of this block's partial are
+  // not stored unless the block gives its part up.
+  const bool own = wsp.od1 > wsp.od0;
+  const int od0 = wsp.od0, od1 = wsp.od1;
   // The own dim tiles, as stored, in eight registers (a uniform switch, so
   // that only these stay live through the wait).
   f32x4 own_v[8];
   if (own) {
     switch (od0 >> 2) {
 #define DCP_OWN_CASE(c) \
-      case c: { _Pragma("unroll") for (int j = 0; j < 8; ++j) own_v[j] = ws_value(oacc[min(4 * c + j, 31)]); } break;
+      case c: { _Pragma("unroll") for (int j = 0; j < 8; ++j) own_v[j] = wsp.value(oacc[min(4 * c + j, 31)]); } break;
       DCP_OWN_CASE(0) DCP_OWN_CASE(1) DCP_OWN_CASE(2) DCP_OWN_CASE(3)
       DCP_OWN_CASE(4) DCP_OWN_CASE(5) DCP_OWN_CASE(6) DCP_OWN_CASE(7)
 #undef DCP_OWN_CASE
       default: break;
     }
   }
-  const unsigned ws_elem = half_ws ? 8u : 16u;    // workspace bytes per 4 dims
-  const __amdgpu_buffer_rsrc_t ws_ro =
-      coherent_rsrc(reinterpret_cast<const char*>(p.ws_o) + (size_t)(blk_part * H + h0) * 128u * ws_elem,
-                    (unsigned)nh * 128u * ws_elem);
-  auto store_ws = [&](int d, const f32x4& o) {
-    const unsigned off = (unsigned)((d * nh + hl) * 4 + g) * ws_elem;
-    if (half_ws) store_coherent2(ws_ro, off, pack_f16x4(o * inv * sc));
-    else store_coherent4(ws_ro, off, o * inv);
-  };
   if (writer) {
     if (to_part) {
       float* po = p.o_part + (((long long)shard * p.rows + row) * H + head) * kVDim;
@@ -319,10 +365,12 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
       for (int d = 0; d < 32; ++d) *reinterpret_cast<f32x4*>(po + 16 * d + 4 * g) = oacc[d] * inv;
       if (g == 0) p.lse_part[((long long)shard * p.rows + row) * H + head] = lse_v;
     }
-    if (to_ws) {
+    if (to_ws && !pre_stored) {
 #pragma unroll
       for (int d = 0; d < 32; ++d)
-        if (d < od0 || d >= od1) store_ws(d, oacc[d]);
+        if (!wsp.is_own(d)) wsp.store(d, oacc[d]);
+    }
+    if (to_ws) {
       if (g == 0) {
         store_coherent(coherent_rsrc(p.ws_lse + blk_part * H, (unsigned)H * 4u),
                        (unsigned)head * 4u, lse_v);
@@ -408,7 +456,7 @@ __device__ inline void finish_block(const DecodeParams& p, long long row, int sh
 #pragma unroll
       for (int j = 0; j < 8; ++j)    // own_v holds the fp16 image: re-packing is exact
         if (od0 + j < od1)
-          store_coherent2(ws_ro, (unsigned)(((od0 + j) * nh + hl) * 4 + g) * 8u, pack_f16x4(own_v[j]));
+          store_coherent2(wsp.r, (unsigned)(((od0 + j) * nh + hl) * 4 + g) * 8u, pack_f16x4(own_v[j]));
     }
     wait_vmcnt<0>();
     __syncthreads();
