@@ -20,14 +20,13 @@
 //
 // Data movement.  A tile is 128 tokens.  Its 576-byte rows are copied from
 // HBM straight into LDS with global->LDS DMA.  Each copy instruction moves
-// one 64-byte granule of 16 tokens.  LDS layout of a stage: [granule G:
-// bytes 64G.. of the row, 9][token / 16 = b][16-byte chunk c of the granule,
-// 4][token % 16, XOR 8 in odd b], then the tile's 128 fp32 token scales.
-// Chunk-major blocks with the odd-block flip keep the 16-byte operand reads
-// of S^T = K Q^T and the 8-byte transposing reads of V^T free of LDS bank
-// conflicts on gfx950 (measured with the SQ bank-conflict counter; the
-// token-major layout with XOR-permuted chunks had two-way conflicts on the
-// S^T reads).  Two stages: tile it+1 streams in while tile it is computed, its
+// one 64-byte granule of 16 tokens, four lanes per granule.  LDS layout of a
+// stage: [granule G: bytes 64G.. of the row, 9][token / 16][token % 16][4 x
+// 16-byte chunks], the chunks of token t permuted by XOR with sw(t) =
+// ((t >> 1) ^ (t >> 3) ^ (t >> 4)) & 3, which keeps the 16-byte operand
+// reads of S^T = K Q^T and the 8-byte transposing reads of V^T free of bank
+// conflicts on 32- and 64-bank LDS alike; then the tile's 128 fp32 token
+// scales.  Two stages: tile it+1 streams in while tile it is computed, its
 // copies issued among the QK MFMAs of tile it.  The slot ids (sparse) or
 // page ids (dense) of tile it+2 are DMA'd into a three-deep ring at the same
 // time, so the row addresses of the next tile are ready without a dependent
@@ -54,6 +53,9 @@ constexpr int kSmem = kRingOff + 3 * kT * 4;       // 150016 bytes
 constexpr int kThreads = 256;
 
 template <bool B> struct BoolC { static constexpr bool value = B; };
+
+// Chunk permutation of token t inside its 64-byte granule.
+__device__ __forceinline__ int chunk_sw(int t) { return ((t >> 1) ^ (t >> 3) ^ (t >> 4)) & 3; }
 
 // Four E4M3 codes (RNE) of four floats, in byte order.
 __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
@@ -119,10 +121,10 @@ void decode_fp8_kernel(const DecodeParams p) {
   };
 
   // ---- copies.  Rows of tile `it` into stage it & 1: wave w fills token
-  // blocks 2w + h (h = 0, 1; 16 tokens each) for all 9 granules; lane l
-  // writes slot l of the block: chunk l / 16 of token 16(2w + h) + (l % 16 ^
-  // 8h).  Waves 0 and 1 also copy the tile's 128 scales (token 64w + lane).
-  const int dma_tok[2] = {32 * wave + (lane & 15), 32 * wave + 16 + ((lane & 15) ^ 8)};
+  // groups 2w and 2w+1 (16 tokens each) for all 9 granules; lane l covers
+  // token 16(2w + h) + l/4 and the 16-byte chunk (l & 3) ^ sw of its granule.
+  // Waves 0 and 1 also copy the tile's 128 scales (token 64w + lane).
+  const int dma_tok = 32 * wave + (lane >> 2);     // + 16h
   const int sc_tok = 64 * (wave & 1) + lane;
   // Tokens past the tile's valid count copy the tile's first token: they are
   // masked out of the softmax, and a real row keeps their V codes finite
@@ -141,18 +143,19 @@ void decode_fp8_kernel(const DecodeParams p) {
     int id[2];
     int sc;
   };
-  const int chunk_off = 16 * (lane >> 4);
+  const int chunk_off0 = 16 * ((lane & 3) ^ chunk_sw(dma_tok));
+  const int chunk_off1 = 16 * ((lane & 3) ^ chunk_sw(dma_tok + 16));
   auto plan_rows = [&](int it, const TileIds& id) {
     RowCopies rc;
     const int tok0 = start + it * kT;
-    rc.prow[0] = pool_row(tok0 + eff(it, dma_tok[0]), id.id[0]);
-    rc.prow[1] = pool_row(tok0 + eff(it, dma_tok[1]), id.id[1]);
+    rc.prow[0] = pool_row(tok0 + eff(it, dma_tok), id.id[0]);
+    rc.prow[1] = pool_row(tok0 + eff(it, dma_tok + 16), id.id[1]);
     rc.prow_sc = pool_row(tok0 + eff(it, sc_tok), id.sc);
     return rc;
   };
   auto issue_copy = [&](const RowCopies& rc, int it, int c) {
     const int h = c & 1, G = c >> 1;
-    const char* src = kvbase + (long long)rc.prow[h] * kRowBytes + chunk_off + 64 * G;
+    const char* src = kvbase + (long long)rc.prow[h] * kRowBytes + (h ? chunk_off1 : chunk_off0) + 64 * G;
     dma16(src, smem + (it & 1) * kStageBytes + (2 * wave + h) * 1024 + G * kGranPlane);
   };
   auto issue_scales = [&](const RowCopies& rc, int it) {
@@ -161,8 +164,8 @@ void decode_fp8_kernel(const DecodeParams p) {
   // Ids of the tokens this lane copies in tile `it`, from the ring.
   auto ring_ids = [&](int it, TileIds& id) {
     const DCP_LDS int* rg = ring + (it % 3) * kT;
-    id.id[0] = rg[eff(it, dma_tok[0])];
-    id.id[1] = rg[eff(it, dma_tok[1])];
+    id.id[0] = rg[eff(it, dma_tok)];
+    id.id[1] = rg[eff(it, dma_tok + 16)];
     id.sc = rg[eff(it, sc_tok)];
   };
   // Ids of tile `it` into ring slot `slot` (waves 2 and 3, 64 tokens each).
@@ -181,8 +184,8 @@ void decode_fp8_kernel(const DecodeParams p) {
   auto id_at = [&](int j) { return load_bounded(id_rsrc, (unsigned)(DENSE ? j / page : j) * 4u); };
   auto tok_cap = [&](int t) { return start + t < cap ? t : 0; };
   TileIds ids0;
-  ids0.id[0] = id_at(start + tok_cap(dma_tok[0]));
-  ids0.id[1] = id_at(start + tok_cap(dma_tok[1]));
+  ids0.id[0] = id_at(start + tok_cap(dma_tok));
+  ids0.id[1] = id_at(start + tok_cap(dma_tok + 16));
   ids0.sc = id_at(start + tok_cap(sc_tok));
   const int id_first = id_at(start);
 
@@ -213,7 +216,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   {
     auto valid0 = [&](int t) { return start + t < end; };
 #pragma unroll
-    for (int h = 0; h < 2; ++h) ids0.id[h] = valid0(dma_tok[h]) ? ids0.id[h] : id_first;
+    for (int h = 0; h < 2; ++h) ids0.id[h] = valid0(dma_tok + 16 * h) ? ids0.id[h] : id_first;
     ids0.sc = valid0(sc_tok) ? ids0.sc : id_first;
   }
   const RowCopies rc0 = plan_rows(0, ids0);
@@ -316,24 +319,29 @@ void decode_fp8_kernel(const DecodeParams p) {
   for (int d = 0; d < 32; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // per-lane LDS offsets (bytes) inside a stage.
-  // QK: S tile st (token block st), latent k-step s, lane (token i16, group
-  // g) reads chunks 2(g & 1) + cc (cc = 0, 1) of granule 2s + (g >> 1) of token
-  // 16st + i16; the RoPE k-step reads chunk g of granule 8.  Index [st & 1].
-  int qk_lat[2][2], qk_rope[2];
+  // QK: S tile st, latent k-step s, lane (token i16, group g) reads chunks
+  // 2(g & 1) + cc (cc = 0, 1) of granule 2s + (g >> 1) of token 16st + i16;
+  // the RoPE k-step reads chunk g of granule 8.  The chunk permutation of
+  // token 16st + i16 is sw0(i16) ^ cst(st).
+  const int sw0 = ((i16 >> 1) ^ (i16 >> 3)) & 3;
+  int qk_lat[2][4], qk_rope[4];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
+  for (int c = 0; c < 4; ++c) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
-      qk_lat[cc][par] = (g >> 1) * kGranPlane + 256 * (2 * (g & 1) + cc) + 16 * (i16 ^ (8 * par));
-    qk_rope[par] = 8 * kGranPlane + 256 * g + 16 * (i16 ^ (8 * par));
+      qk_lat[cc][c] = (g >> 1) * kGranPlane + 64 * i16 + 16 * ((2 * (g & 1) + cc) ^ sw0 ^ c);
+    qk_rope[c] = 8 * kGranPlane + 64 * i16 + 16 * (g ^ sw0 ^ c);
   }
   // PV: tr8 read r of lane L (group g) fetches token 32r + 16(jj >= 4) + 4g +
-  // (jj & 3), jj = L/2 (token block 2r + (jj >= 4)), bytes 8(L & 1) of chunk
-  // d & 3 of granule d >> 2: lane i of the group then holds dim 16d + i of the
-  // 8 tokens of k-slots 8r..8r+7.
+  // (jj & 3), jj = L/2, bytes 8(L & 1) of chunk d & 3 of granule d >> 2: lane i
+  // of the group then holds dim 16d + i of the 8 tokens of k-slots 8r..8r+7.
+  // That token's chunk permutation is swl ^ 2(r & 1).
   const int jj = i16 >> 1;
   const int pv_hi = jj >> 2, pv_p = 4 * g + (jj & 3);
-  const int pv_base = 1024 * pv_hi + 16 * (pv_p ^ (8 * pv_hi)) + 8 * (i16 & 1);
+  const int swl = ((pv_p >> 1) ^ (pv_p >> 3) ^ (3 * pv_hi)) & 3;
+  int pv_off[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) pv_off[v] = 1024 * pv_hi + 64 * pv_p + 8 * (i16 & 1) + 16 * (v ^ swl);
   // softmax: the scales of tokens 16st + 4g .. +3
   const int sc_off = kTileBytes + 16 * g;
 
@@ -394,12 +402,13 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           const int st = 4 * half + q;
+          const int cst = ((2 * st) ^ st) & 3;
           if (s < 4) {
-            const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[0][st & 1] + 2 * s * kGranPlane + 1024 * st);
-            const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[1][st & 1] + 2 * s * kGranPlane + 1024 * st);
+            const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[0][cst] + 2 * s * kGranPlane + 1024 * st);
+            const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[1][cst] + 2 * s * kGranPlane + 1024 * st);
             a[q] = i32x8{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
           } else {
-            const i32x4 r4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_rope[st & 1] + 1024 * st);
+            const i32x4 r4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_rope[cst] + 1024 * st);
             a[q] = i32x8{r4.x, r4.y, r4.z, r4.w, r4.x, r4.y, r4.z, r4.w};
           }
         }
@@ -455,7 +464,7 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < NR; ++r)
         r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (DCP_LDS i32x2*)(sb + (d >> 2) * kGranPlane + 2048 * r + 256 * (d & 3) + pv_base));
+            (DCP_LDS i32x2*)(sb + (d >> 2) * kGranPlane + 2048 * r + pv_off[(d & 3) ^ (2 * (r & 1))]));
     };
 #pragma unroll
     for (int j = 0; j < 2; ++j) load_v(j, vr[0][j]);
