@@ -388,6 +388,7 @@ void decode_fp8_kernel(const DecodeParams p) {
 
     // ---- S^T = K Q^T (base-2 logits), eight 16-token S tiles in two passes of four
     f32x4 sacc[NS];
+    i32x8 a[NQ];
 #pragma unroll
     for (int half = 0; half < NH; ++half) {
       if (half == 1 && short_tile) {       // S tiles 4..7 are all masked
@@ -398,25 +399,27 @@ void decode_fp8_kernel(const DecodeParams p) {
       f32x4 acc[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto load_k = [&](int s, i32x8* a) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int st = 4 * half + q;
-          const int cst = ((2 * st) ^ st) & 3;
-          if (s < 4) {
-            const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[0][cst] + 2 * s * kGranPlane + 1024 * st);
-            const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[1][cst] + 2 * s * kGranPlane + 1024 * st);
-            a[q] = i32x8{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-          } else {
-            const i32x4 r4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_rope[cst] + 1024 * st);
-            a[q] = i32x8{r4.x, r4.y, r4.z, r4.w, r4.x, r4.y, r4.z, r4.w};
-          }
+      // Operand of S tile 4 half + q for k-step s.
+      auto load_kq = [&](int hf, int s, int q) -> i32x8 {
+        const int st = 4 * hf + q;
+        const int cst = ((2 * st) ^ st) & 3;
+        if (s < 4) {
+          const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[0][cst] + 2 * s * kGranPlane + 1024 * st);
+          const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_lat[1][cst] + 2 * s * kGranPlane + 1024 * st);
+          return i32x8{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
         }
+        const i32x4 r4 = *reinterpret_cast<const DCP_LDS i32x4*>(sb + qk_rope[cst] + 1024 * st);
+        return i32x8{r4.x, r4.y, r4.z, r4.w, r4.x, r4.y, r4.z, r4.w};
       };
-      // One operand set: step s + 1 is loaded once step s's MFMAs are
-      // issued (they have eight MFMAs of work queued to cover the latency).
-      i32x8 a[NQ];
-      load_k(0, a);
+      // One operand set, rolled: the operand of S tile q for the next k-step
+      // is loaded as soon as q's MFMAs of this k-step are issued, so it has
+      // the rest of the k-step to arrive.  (Half 0's RoPE step loads half 1's
+      // first operands.)
+      if (half == 0) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) a[q] = load_kq(0, 0, q);
+      }
+      const bool more = half == 0 && !short_tile;
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
         // Before k-step s + 1 is loaded: at s = 1 granules 4..7 (copies up to
@@ -433,24 +436,34 @@ void decode_fp8_kernel(const DecodeParams p) {
         }
         if (s < 4) {
 #pragma unroll
-          for (int q = 0; q < NQ; ++q)
-            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qhi[s], acc[q], 0, 0,
-                                                                     0, 127, 0, qscale);
+          for (int q = 0; q < NQ; q += 2) {
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qhi[s], acc[q], 0, 0, 0, 127, 0, qscale);
+            acc[q + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q + 1], qhi[s], acc[q + 1], 0, 0, 0, 127, 0, qscale);
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qlo[s], acc[q], 0, 0, 0, 127, 0, qscale);
+            a[q] = load_kq(half, s + 1, q);
+            acc[q + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q + 1], qlo[s], acc[q + 1], 0, 0, 0, 127, 0, qscale);
+            a[q + 1] = load_kq(half, s + 1, q + 1);
+          }
+          // issue order: per pair of S tiles three MFMAs, q's next operand,
+          // one MFMA, q + 1's next operand
 #pragma unroll
-          for (int q = 0; q < NQ; ++q)
-            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qlo[s], acc[q], 0, 0,
-                                                                     0, 127, 0, qscale);
+          for (int q = 0; q < NQ; q += 2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
         } else {
 #pragma unroll
-          for (int q = 0; q < NQ; ++q)
-            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qr, acc[q], 0, 0,
-                                                                     0, 127, 0, qscale);
+          for (int q = 0; q < NQ; ++q) {
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qr, acc[q], 0, 0, 0, 127, 0, qscale);
+            if (more) a[q] = load_kq(1, 0, q);
+          }
         }
         if constexpr (next) {
           const int j = 5 * half + s;
           if (j < 9) issue_copy(rc, it + 1, j);
         }
-        if (s + 1 < 5) load_k(s + 1, a);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
