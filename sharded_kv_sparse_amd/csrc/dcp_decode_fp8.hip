@@ -626,6 +626,9 @@ void decode_fp8_kernel(const DecodeParams p) {
         if constexpr (!next) {
           if (grp > 0) store_pair(grp - 1);
         }
+        // issue order: the next pair's V^T reads first, then this pair's MFMAs
+        if (grp + 1 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, sh ? 4 : 6, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (!next) store_pair(15);
