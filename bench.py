@@ -79,8 +79,8 @@ METRIC = "µs/layer-step and KV HBM GB/s (% of peak), sparse MLA decode B=64 top
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="sparse_fp8_b64_k2048", choices=sorted(wl.PRESETS))
     ap.add_argument("--groups", type=int, default=4, help="table groups (4 layers each) rotated")
     ap.add_argument("--layers-per-table", type=int, default=4)
