@@ -174,25 +174,18 @@ void decode_fp8_kernel(const DecodeParams p) {
     dma4(id_ptr(start + it * kT + eff(it, t)), ring + slot * kT + (wave - 2) * 64);
   };
 
-  // ---- tile 0's ids.  For split 0 their loads do not wait for the count:
-  // they are bounded by the id table (cap entries) instead, and the ids of
-  // tokens past the count are replaced by the first token's once the count
-  // is known, when the copies are planned.
+  // ---- tile 0's ids go into ring slot 0 by DMA (waves 2 and 3, like every
+  // ring slot), and the query right behind them, so that neither waits for
+  // the other's latency.  For split 0 the ids do not wait for the count: they
+  // are bounded by the id table (cap entries) instead, and the ids of tokens
+  // past the count are replaced by the first token's once the count is
+  // known, when the copies are planned.
   const int cap = DENSE ? p.max_pages * p.page_size : p.k;
-  const __amdgpu_buffer_rsrc_t id_rsrc =
-      coherent_rsrc(ids, (unsigned)(DENSE ? p.max_pages : p.k) * 4u);
-  auto id_at = [&](int j) { return load_bounded(id_rsrc, (unsigned)(DENSE ? j / page : j) * 4u); };
   auto tok_cap = [&](int t) { return start + t < cap ? t : 0; };
-  TileIds ids0;
-  ids0.id[0] = id_at(start + tok_cap(dma_tok));
-  ids0.id[1] = id_at(start + tok_cap(dma_tok + 16));
-  ids0.sc = id_at(start + tok_cap(sc_tok));
-  const int id_first = id_at(start);
-
-  touch(ids0.id[0]);
-  touch(ids0.id[1]);
-  touch(ids0.sc);
-  touch(id_first);
+  if (wave >= 2 && start < cap) {
+    const int t = (wave - 2) * 64 + lane;
+    dma4(id_ptr(start + tok_cap(t)), ring + (wave - 2) * 64);
+  }
 
   // ---- the query of the wave's 16 heads (18 KB, contiguous) is copied into
   // stage 1, idle until tile 1's copies, by the same global->LDS DMA as the
@@ -209,6 +202,13 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < kQWaveBytes / 1024; ++i) dma16(qw + 1024 * i + 16 * lane, q_lds + 1024 * i);
   }
+  if (wave >= 2) wait_vmcnt<18>();     // the ids (the query stays in flight)
+  lds_barrier();
+  TileIds ids0;
+  ids0.id[0] = ring[dma_tok];
+  ids0.id[1] = ring[dma_tok + 16];
+  ids0.sc = ring[sc_tok];
+  const int id_first = ring[0];
 
   // ---- tile 0: the scales (waves 0, 1) or the ids of tile 1 (waves 2, 3)
   // first, as at the top of every tile, then all its copies.
