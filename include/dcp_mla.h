@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DCP_ABI_VERSION 1
+#define DCP_ABI_VERSION 2
 #define DCP_HEAD_DIM 576
 #define DCP_V_DIM 512
 #define DCP_MAX_SHARDS 16
@@ -71,13 +71,27 @@ typedef enum dcp_out_dtype {
                             the prefix merge: fp32 arithmetic, BF16 storage)      */
 } dcp_out_dtype;
 
-/* One shard's paged latent KV cache (device pointers). */
+/*
+ * One shard's paged latent KV cache (device pointers).  Pool row r (576
+ * bf16 values, or 576 E4M3FN codes) starts at (char*)kv + r * row_stride;
+ * the fp32 scale of an FP8 row r sits at (char*)kv_scale + r * scale_stride.
+ * The scale may live inside the row's own padding: with row_stride = 640
+ * and kv_scale = (char*)kv + 576, scale_stride = 640, a 128-byte-aligned
+ * row spans exactly five 128-byte lines, scale included, where separate
+ * 576-byte rows and a scale array touch six (five for the row, one for the
+ * scale).  Requirements (else DCP_ERR_INVALID_ARGUMENT): kv 16-byte aligned;
+ * row_stride 0 (packed: 576 FP8 / 1152 BF16) or a multiple of 16 no smaller
+ * than the row; kv_scale 4-byte aligned; scale_stride 0 (packed fp32 array)
+ * or a positive multiple of 4.
+ */
 typedef struct dcp_kv_shard {
-  const void* kv;           /* [pool_rows, 576] bf16, or uint8 E4M3FN codes      */
-  const float* kv_scale;    /* [pool_rows] fp32 per-token scale (FP8); NULL for BF16 */
+  const void* kv;           /* pool rows, bf16 or uint8 E4M3FN codes               */
+  const float* kv_scale;    /* per-token fp32 scales (FP8); NULL for BF16          */
   int64_t pool_rows;        /* rows in this shard's pool = physical pages * page  */
   const int32_t* local_len; /* dense only: [num_seqs] tokens of each sequence held
                                by this shard (0 = none); NULL for sparse          */
+  int64_t row_stride;       /* bytes from one pool row to the next (0 = packed)   */
+  int64_t scale_stride;     /* bytes from one scale to the next (0 = 4)           */
 } dcp_kv_shard;
 
 /* Human-readable name of a status code (static storage). */

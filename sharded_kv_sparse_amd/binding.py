@@ -14,6 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdcpmla.so")
 
+ABI_VERSION = 2           # DCP_ABI_VERSION this binding's structures follow
 HEAD_DIM = 576
 V_DIM = 512
 MAX_SHARDS = 16
@@ -37,7 +38,8 @@ class DcpError(RuntimeError):
 
 class KvShard(ctypes.Structure):
     _fields_ = [("kv", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
-                ("pool_rows", ctypes.c_int64), ("local_len", ctypes.c_void_p)]
+                ("pool_rows", ctypes.c_int64), ("local_len", ctypes.c_void_p),
+                ("row_stride", ctypes.c_int64), ("scale_stride", ctypes.c_int64)]
 
 
 _lib = None
@@ -71,6 +73,9 @@ def lib():
     L.mla_dense_decode_lse.restype = ctypes.c_int
     L.lse_combine.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, ctypes.c_int, vp]
     L.lse_combine.restype = ctypes.c_int
+    if L.dcp_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.dcp_abi_version()}, the binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     _lib = L
     return L
 
@@ -90,14 +95,14 @@ def _stream(device, stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _need(t, dtype, name, shape=None):
+def _need(t, dtype, name, shape=None, contiguous=True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
@@ -163,19 +168,23 @@ def _shards(pools, scales, local_lens=None):
     for r, pool in enumerate(pools):
         if pool.dtype != pools[0].dtype:
             raise TypeError("all shards share one KV dtype")
-        _need(pool, pool.dtype, f"pool[{r}]")
-        if pool.dim() != 2 or pool.shape[1] != HEAD_DIM:
-            raise ValueError(f"pool[{r}] must be [rows, {HEAD_DIM}]")
+        # pools may be row-strided views (rows padded, e.g. with the scale
+        # inside), scales strided views; the library checks the alignment
+        _need(pool, pool.dtype, f"pool[{r}]", contiguous=False)
+        if pool.dim() != 2 or pool.shape[1] != HEAD_DIM or pool.stride(1) != 1:
+            raise ValueError(f"pool[{r}] must be [rows, {HEAD_DIM}] with unit inner stride")
         sc = None
         if kv_dtype == KV_FP8_E4M3:
             sc = scales[r]
-            _need(sc, torch.float32, f"scale[{r}]", (pool.shape[0],))
+            _need(sc, torch.float32, f"scale[{r}]", (pool.shape[0],), contiguous=False)
         ll = None
         if local_lens is not None:
             ll = local_lens[r]
             _need(ll, torch.int32, f"local_len[{r}]")
         arr[r] = KvShard(pool.data_ptr(), None if sc is None else sc.data_ptr(), pool.shape[0],
-                         None if ll is None else ll.data_ptr())
+                         None if ll is None else ll.data_ptr(),
+                         pool.stride(0) * pool.element_size(),
+                         0 if sc is None else sc.stride(0) * 4)
     return arr, kv_dtype
 
 

@@ -98,6 +98,15 @@ dcp_status check_shards(const dcp_kv_shard* shards, int num_shards, dcp_kv_dtype
     const dcp_kv_shard& s = shards[r];
     if (!s.kv || s.pool_rows < 1) return DCP_ERR_INVALID_ARGUMENT;
     if (kv_dtype == DCP_KV_FP8_E4M3 && !s.kv_scale) return DCP_ERR_INVALID_ARGUMENT;
+    // every row is copied in 16-byte pieces, every scale in 4 bytes
+    const long long row_bytes = kv_dtype == DCP_KV_FP8_E4M3 ? kHeadDim : 2 * kHeadDim;
+    if (reinterpret_cast<uintptr_t>(s.kv) % 16 != 0) return DCP_ERR_INVALID_ARGUMENT;
+    if (s.row_stride != 0 && (s.row_stride < row_bytes || s.row_stride % 16 != 0))
+      return DCP_ERR_INVALID_ARGUMENT;
+    if (kv_dtype == DCP_KV_FP8_E4M3) {
+      if (reinterpret_cast<uintptr_t>(s.kv_scale) % 4 != 0) return DCP_ERR_INVALID_ARGUMENT;
+      if (s.scale_stride < 0 || s.scale_stride % 4 != 0) return DCP_ERR_INVALID_ARGUMENT;
+    }
     if (dense && !s.local_len) return DCP_ERR_INVALID_ARGUMENT;
   }
   return DCP_OK;
@@ -174,6 +183,10 @@ DecodeParams make_params(const CommonArgs& a, const WorkspacePlan& w) {
     p.shard[r].kv = a.shards[r].kv;
     p.shard[r].scale = a.shards[r].kv_scale;
     p.shard[r].pool_rows = a.shards[r].pool_rows;
+    p.shard[r].row_stride = a.shards[r].row_stride != 0
+                                ? a.shards[r].row_stride
+                                : (a.kv_dtype == DCP_KV_FP8_E4M3 ? kHeadDim : 2 * kHeadDim);
+    p.shard[r].scale_stride = a.shards[r].scale_stride != 0 ? a.shards[r].scale_stride : 4;
     p.shard[r].local_len = a.shards[r].local_len;
   }
   p.rows = a.rows;

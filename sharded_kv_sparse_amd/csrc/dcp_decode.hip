@@ -228,12 +228,13 @@ void decode_kernel(const DecodeParams p) {
       const int pch = lc - t * CPR;
       const long long prow = pool_row(tok0 + (t < nval ? t : 0));
       const int c = pch ^ swz<FP8>(t);
-      dma16(kvbase + prow * RB + c * 16, sbase + blk * 1024);
+      dma16(kvbase + prow * sh.row_stride + c * 16, sbase + blk * 1024);
     }
     if constexpr (FP8) {
       if (wave == 0) {
         const long long prow = pool_row(tok0 + (lane < nval ? lane : 0));
-        dma4(sh.scale + prow, sbase + kTileBytes);
+        dma4(reinterpret_cast<const float*>(reinterpret_cast<const char*>(sh.scale) + prow * sh.scale_stride),
+             sbase + kTileBytes);
       }
     }
   };

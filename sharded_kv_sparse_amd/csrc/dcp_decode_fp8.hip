@@ -43,7 +43,6 @@ namespace dcp {
 namespace {
 
 constexpr int kT = 128;                            // tokens per tile
-constexpr int kRowBytes = 576;                     // E4M3 codes per key row
 constexpr int kGranules = 9;                       // 64-byte granules per row
 constexpr int kGranPlane = kT * 64;                // LDS bytes of one granule plane
 constexpr int kTileBytes = kGranules * kGranPlane; // 73728
@@ -93,6 +92,7 @@ void decode_fp8_kernel(const DecodeParams p) {
 
   const ShardArg sh = p.shard[shard];
   const char* kvbase = static_cast<const char*>(sh.kv);
+  const char* scbase = reinterpret_cast<const char*>(sh.scale);
   const int max_prow = (int)min(sh.pool_rows - 1, (long long)0x7fffffff);
 
   // ---- this block's token range [start, end) of the shard's local tokens
@@ -155,11 +155,13 @@ void decode_fp8_kernel(const DecodeParams p) {
   };
   auto issue_copy = [&](const RowCopies& rc, int it, int c) {
     const int h = c & 1, G = c >> 1;
-    const char* src = kvbase + (long long)rc.prow[h] * kRowBytes + (h ? chunk_off1 : chunk_off0) + 64 * G;
+    const char* src = kvbase + (long long)rc.prow[h] * sh.row_stride + (h ? chunk_off1 : chunk_off0) + 64 * G;
     dma16(src, smem + (it & 1) * kStageBytes + (2 * wave + h) * 1024 + G * kGranPlane);
   };
   auto issue_scales = [&](const RowCopies& rc, int it) {
-    if (wave < 2) dma4(sh.scale + rc.prow_sc, smem + (it & 1) * kStageBytes + kTileBytes + 256 * wave);
+    if (wave < 2)
+      dma4(reinterpret_cast<const float*>(scbase + (long long)rc.prow_sc * sh.scale_stride),
+           smem + (it & 1) * kStageBytes + kTileBytes + 256 * wave);
   };
   // Ids of the tokens this lane copies in tile `it`, from the ring.
   auto ring_ids = [&](int it, TileIds& id) {

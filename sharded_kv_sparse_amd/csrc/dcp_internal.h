@@ -23,6 +23,8 @@ struct ShardArg {
   const float* scale;
   long long pool_rows;
   const int* local_len;
+  long long row_stride;          // bytes between pool rows (resolved, never 0)
+  long long scale_stride;        // bytes between FP8 scales (resolved, never 0)
 };
 
 struct DecodeParams {

@@ -20,6 +20,10 @@ top-k 2048 sparse decode, MTP rows, million-token dense contexts):
 * Q ~ N(0,1) rounded to bfloat16.  BF16 KV ~ N(0,1) rounded to bfloat16.  FP8
   KV codes are N(0,1) rounded to E4M3FN by torch's conversion; the per-token
   fp32 scale is 2^U(-6, 2).
+* FP8 pools come in two layouts with the same values: 576-byte rows plus a
+  separate fp32 scale array, or (row_bytes = 640) each row padded to 640
+  bytes with its scale in bytes 576..579 (the pool and scale tensors are then
+  strided views of one buffer).
 """
 
 from dataclasses import dataclass, field, replace
@@ -49,6 +53,7 @@ class Preset:
     mtp_empty_rows: bool = False   # sparse MTP: constructed zero-slot rows
     forced_empty: bool = False     # dense: one shard empty for b mod 4 == 0
     short_rows: int = 0       # sparse: if > 0, rows keep 1..short_rows valid slots
+    row_bytes: int = 0        # FP8: 0 = 576-byte rows + scale array; 640 = scale in the row
     sigma: float = 1.0 / math.sqrt(192.0)
     seed: int = 0
     note: str = ""
@@ -180,8 +185,10 @@ def _generator(device, seed):
     return g
 
 
-def _fill_kv(rows, kv_dtype, device, gen, chunk_rows=1 << 17):
-    if kv_dtype == "bf16":
+def _fill_kv(rows, kv_dtype, device, gen, chunk_rows=1 << 17, out=None):
+    if out is not None:
+        pass
+    elif kv_dtype == "bf16":
         out = torch.empty((rows, D_K), dtype=torch.bfloat16, device=device)
     else:
         out = torch.empty((rows, D_K), dtype=torch.uint8, device=device)
@@ -215,7 +222,7 @@ class Workload:
         return self.q.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
     def pool_host(self, layer, r):
-        t = self.pools[layer][r].detach().cpu()
+        t = self.pools[layer][r].detach().cpu().contiguous()
         if self.p.kv_dtype == "bf16":
             return t.view(torch.int16).numpy().view(np.uint16)
         return t.numpy()
@@ -241,11 +248,22 @@ def make_workload(p, device="cpu", layers=1, seed=None):
         lgen = _generator(device, seed * 1000 + layer + 1)
         pools, scales, scales_h = [], [], []
         for _ in range(p.num_shards):
-            pools.append(_fill_kv(p.pool_rows, p.kv_dtype, device, lgen))
+            inline = p.kv_dtype == "fp8" and p.row_bytes > 0
+            if inline:
+                assert p.row_bytes % 16 == 0 and p.row_bytes >= D_K + 4
+                buf = torch.zeros((p.pool_rows, p.row_bytes), dtype=torch.uint8, device=device)
+                pools.append(_fill_kv(p.pool_rows, p.kv_dtype, device, lgen, out=buf[:, :D_K]))
+            else:
+                pools.append(_fill_kv(p.pool_rows, p.kv_dtype, device, lgen))
             if p.kv_dtype == "fp8":
                 s = make_scales(p, rng)
                 scales_h.append(s)
-                scales.append(torch.from_numpy(s).to(device))
+                if inline:
+                    sc = buf.view(torch.float32)[:, D_K // 4]
+                    sc.copy_(torch.from_numpy(s).to(device))
+                    scales.append(sc)
+                else:
+                    scales.append(torch.from_numpy(s).to(device))
             else:
                 scales_h.append(None)
                 scales.append(None)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.dcp_abi_version() == 1
+    assert L.dcp_abi_version() == 2
     for code, name in B.STATUS_NAMES.items():
         assert L.dcp_status_string(code).decode() == name
     assert L.dcp_status_string(99).decode() == "DCP_ERR_UNKNOWN"
@@ -102,6 +102,25 @@ def test_sparse_decode_argument_checks(L):
     assert _sparse(L, ws=None, ws_bytes=0) == WS_SMALL             # merged output needs counters
     assert _sparse(L, ws_bytes=16) == WS_SMALL
     assert _sparse(L, rows=0, q=None, shards=None, local=None, counts=None) == OK
+
+
+def test_kv_layout_checks(L):
+    # row and scale strides: alignment and size rules of the dcp_kv_shard layout
+    def sh(kv=0x20000, scale=0x30000, row_stride=0, scale_stride=0):
+        arr = (B.KvShard * 2)()
+        for r in range(2):
+            arr[r] = B.KvShard(kv, scale, 1024, None, row_stride, scale_stride)
+        return arr
+    fp8 = B.KV_FP8_E4M3
+    assert _sparse(L, kv=fp8, shards=sh(row_stride=600)) == INVALID     # not a multiple of 16
+    assert _sparse(L, kv=fp8, shards=sh(row_stride=560)) == INVALID     # shorter than a row
+    assert _sparse(L, kv=fp8, shards=sh(row_stride=-640)) == INVALID
+    assert _sparse(L, kv=fp8, shards=sh(kv=0x20008)) == INVALID         # kv not 16-byte aligned
+    assert _sparse(L, kv=fp8, shards=sh(scale=0x30002)) == INVALID      # scale not 4-byte aligned
+    assert _sparse(L, kv=fp8, shards=sh(scale_stride=6)) == INVALID
+    assert _sparse(L, kv=fp8, shards=sh(scale_stride=-4)) == INVALID
+    assert _sparse(L, shards=sh(scale=None, row_stride=1136)) == INVALID   # BF16 rows are 1152 bytes
+    assert _sparse(L, shards=sh(scale=None, row_stride=640)) == INVALID
 
 
 def test_dense_decode_argument_checks(L):

@@ -328,3 +328,55 @@ def test_dense_million_token_sampled(gpu):
     ref = oracle_dense(w, rows=rows, heads=heads, host=host)
     err = check_against_oracle(res, ref, "dense 1M", rows=rows, heads=heads)
     say(f"dense 1M: {err}")
+
+
+@pytest.mark.parametrize("kv,heads", [("fp8", 64), ("fp8", 128), ("fp8", 32), ("bf16", 64)])
+def test_strided_pool_layout_is_bit_identical(gpu, kv, heads):
+    # The same codes and scales in packed rows (+ a scale array) and in padded
+    # rows with the scale inside (FP8: 640-byte rows, scale at byte 576; BF16:
+    # 1280-byte rows): identical outputs, partials and LSEs, and both within
+    # tolerance of the oracle.
+    p = wl.Preset("layout", "sparse", kv, batch=6, q_per_seq=1, heads=heads, context=9000,
+                  num_shards=4, topk=700, pad_tail=13, seed=31)
+    w = make(p)
+    packed = gpu_sparse(w)
+    pools, scales = [], []
+    for r in range(p.num_shards):
+        src = w.pools[0][r]
+        rb = 640 if kv == "fp8" else 1280
+        buf = torch.zeros((src.shape[0], rb), dtype=torch.uint8, device=gpu)
+        if kv == "fp8":
+            buf[:, :576] = src
+            sc = buf.view(torch.float32)[:, 144]
+            sc.copy_(w.scales[0][r])
+            pools.append(buf[:, :576])
+            scales.append(sc)
+        else:
+            bv = buf.view(torch.bfloat16)
+            bv[:, :576] = src
+            pools.append(bv[:, :576])
+            scales.append(None)
+    assert pools[0].stride(0) * pools[0].element_size() == (640 if kv == "fp8" else 1280)
+    local, counts = B.remap_topk(w.dev(w.table), p.num_shards)
+    say(f"strided layout {kv} heads={heads}")
+    strided = B.sparse_decode(w.q, pools, scales, local, counts, p.sigma, want_partials=True,
+                              want_merged=True)
+    torch.cuda.synchronize()
+    for key in ("o", "lse", "o_part", "lse_part"):
+        assert torch.equal(packed[key], strided[key]), key
+    check_against_oracle(strided, oracle_sparse(w), f"strided {kv} {heads}")
+
+
+def test_inline_scale_workload_layout(gpu):
+    # The workload generator's 640-byte-row layout (scale inside the row) at a
+    # few-tile size: pool and scale are strided views of one buffer, and the
+    # result matches the oracle on the same values.
+    p = wl.Preset("inline", "sparse", "fp8", batch=5, q_per_seq=1, heads=64, context=12000,
+                  num_shards=4, topk=900, pad_tail=40, seed=37, row_bytes=640)
+    w = make(p)
+    assert w.pools[0][0].stride(0) == 640 and w.scales[0][0].stride(0) == 160
+    assert w.pools[0][0].data_ptr() + 576 == w.scales[0][0].data_ptr()
+    say("inline-scale workload")
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    check_against_oracle(res, oracle_sparse(w), "inline scale")
