@@ -19,4 +19,8 @@ from .dcp_oracle import (  # noqa: F401
     unsharded_sparse,
     unsharded_dense,
     attend,
+    E4M3_MAX,
+    encode_e4m3fn,
+    quantize_row_e4m3,
+    kv_write,
 )

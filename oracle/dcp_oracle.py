@@ -292,3 +292,88 @@ def unsharded_dense(q, pools, kv_dtype, scales, block_table, local_lens, page_si
         ]
         o[b], lse[b] = attend(q[b], np.concatenate(parts, axis=0), sigma)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Interleaved KV-cache write with FP8 quantisation
+# ---------------------------------------------------------------------------
+#
+# [P1] "feat: support decode context parallelism for PyTorch MLA", File
+# summaries: the KV-cache fill kernel writes the new tokens interleaved over
+# the DCP ranks.  [P2] "Feat[DCP] Support decode context parallelism for DSA
+# models with the flashmla_kv backend", summary (FP8 KV caches are packed FP8)
+# and the review of the gathered buffer (rows are quantised when they are
+# written to the persistent cache).  The pages do not give the scale rule;
+# the reading taken here: one fp32 scale per token, the largest magnitude of
+# its 576 values divided by 448 (the largest E4M3FN value), computed in fp32
+# as the kernel does, and 1 for an all-zero token; code = E4M3FN of
+# x / scale rounded to nearest even, in fp32 (a quantised code is an integer
+# decided by floating point, so both sides decide it in the same precision).
+
+E4M3_MAX = 448.0
+
+
+def encode_e4m3fn(values):
+    """float32 values with |v| <= 448 -> OCP E4M3FN codes (uint8), rounding to
+    nearest, ties to even, from the bit definition (the inverse of
+    decode_e4m3fn on its grid).  -0.0 keeps its sign bit."""
+    v = np.asarray(values, dtype=np.float32).astype(np.float64)
+    if np.any(~np.isfinite(v)) or np.any(np.abs(v) > E4M3_MAX):
+        raise ValueError("encode_e4m3fn takes finite values with |v| <= 448")
+    sign = np.signbit(v)
+    a = np.abs(v)
+    codes = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6                               # below the smallest normal
+    # subnormal grid: m * 2^-9, m = 0..7 (m = 8 is the smallest normal, code 8)
+    codes[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)      # rint: ties to even
+    nrm = ~sub
+    if np.any(nrm):
+        mant, ex = np.frexp(a[nrm])                   # a = mant * 2^ex, mant in [0.5, 1)
+        e = ex - 1                                    # a = (2 mant) * 2^e, 2 mant in [1, 2)
+        m8 = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)   # exact operand, ties to even
+        carry = m8 == 8
+        e = np.where(carry, e + 1, e)
+        m8 = np.where(carry, 0, m8)
+        codes[nrm] = ((e + 7) << 3) | m8
+    codes = codes | np.where(sign, 0x80, 0)
+    return codes.astype(np.uint8)
+
+
+def quantize_row_e4m3(x_bits):
+    """One token's 576 bfloat16 values (bit patterns) -> (codes uint8 [576],
+    scale float32): scale = amax / 448 in fp32 (1 when amax is 0), code =
+    E4M3FN(x / scale) with the fp32 quotient clamped to +-448."""
+    x = decode_bf16(x_bits).astype(np.float32)        # exact: a bf16 fits in fp32
+    amax = np.float32(np.max(np.abs(x)))
+    scale = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    q = (x / scale).astype(np.float32)                # IEEE fp32 division per element
+    q = np.clip(q, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return encode_e4m3fn(q), scale
+
+
+def kv_write(kv_new_bits, slots, num_shards, pools, scales, kv_dtype):
+    """Write new tokens into the shards' pools: token i with global slot
+    g = slots[i] >= 0 goes to row g div N of shard g mod N (interleave 1, the
+    same slot naming as remap_topk); a negative slot is skipped.  BF16 pools
+    get the bit patterns as they are; FP8 pools get quantize_row_e4m3's codes
+    and scale.  Returns new lists (the inputs are not modified)."""
+    kv_new_bits = np.asarray(kv_new_bits, dtype=np.uint16)
+    slots = np.asarray(slots, dtype=np.int64)
+    assert kv_new_bits.ndim == 2 and kv_new_bits.shape[1] == D_K
+    assert slots.shape == (kv_new_bits.shape[0],)
+    pools = [np.array(p, copy=True) for p in pools]
+    scales = [None if s is None else np.array(s, copy=True) for s in scales]
+    valid = slots[slots >= 0]
+    assert len(np.unique(valid)) == len(valid), "slots must be distinct"
+    for i, g in enumerate(slots):
+        if g < 0:
+            continue
+        r, row = int(g % num_shards), int(g // num_shards)
+        assert row < pools[r].shape[0], "slot beyond the shard's pool"
+        if kv_dtype == "bf16":
+            pools[r][row] = kv_new_bits[i]
+        else:
+            codes, sc = quantize_row_e4m3(kv_new_bits[i])
+            pools[r][row] = codes
+            scales[r][row] = sc
+    return pools, scales

@@ -15,6 +15,7 @@ import oracle
 import oracle.dcp_oracle as real
 
 from . import test_oracle as pins
+from . import test_oracle_kvwrite as kv_pins
 
 MUTATIONS = [
     ("value slice", "keys[:, :D_V]) / l", "keys[:, -D_V:]) / l"),
@@ -36,12 +37,23 @@ MUTATIONS = [
      "o = contrib.sum(axis=0) / w_sum[..., None]"),
     ("empty shard weighted", "contrib = np.where(valid[..., None], o_parts, 0.0) * w[..., None]",
      "contrib = o_parts * w[..., None]"),
+    ("E4M3 encode bias", "codes[nrm] = ((e + 7) << 3) | m8", "codes[nrm] = ((e + 8) << 3) | m8"),
+    ("E4M3 encode truncates", "m8 = np.rint((2.0 * mant - 1.0) * 8.0)", "m8 = np.floor((2.0 * mant - 1.0) * 8.0)"),
+    ("E4M3 encode no carry", "carry = m8 == 8", "carry = m8 == 9"),
+    ("E4M3 encode subnormal step", "np.rint(a[sub] * 2.0 ** 9)", "np.rint(a[sub] * 2.0 ** 8)"),
+    ("quant scale inverted", "scale = np.float32(amax / np.float32(E4M3_MAX))",
+     "scale = np.float32(np.float32(E4M3_MAX) / amax)"),
+    ("kv write shard by div", "r, row = int(g % num_shards), int(g // num_shards)",
+     "r, row = int(g // num_shards) % num_shards, int(g % num_shards)"),
+    ("kv write keeps skipped", "        if g < 0:\n            continue\n        r, row",
+     "        if g < -1:\n            continue\n        r, row"),
 ]
 
 
 def _pin_calls():
     calls = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+    for name, fn in inspect.getmembers(pins, inspect.isfunction) + \
+            inspect.getmembers(kv_pins, inspect.isfunction):
         if not name.startswith("test_"):
             continue
         marks = getattr(fn, "pytestmark", [])
