@@ -125,6 +125,44 @@ def flops(p, tokens):
     return 2.0 * p.heads * tokens * (576 + 512)
 
 
+def measure_kv_write(w, stream, dev, reps=50):
+    """Time dcp_kv_write on layer 0 of group w: the new tokens of one decode
+    step (q_per_seq per sequence) and a 2048-token chunk per sequence, both
+    at the sequences' last positions; K launches back to back between two
+    events on the launch stream.  Algorithmic bytes per token: the bf16 row
+    read (1152), its slot (4) and the row written (580 FP8 with its scale,
+    1152 BF16)."""
+    p = w.p
+    per_tok = 1152 + 4 + (580 if p.kv_dtype == "fp8" else 1152)
+    out = {"kernel": "kv_write_kernel (interleaved KV-cache write"
+                     + (", E4M3FN quantisation)" if p.kv_dtype == "fp8" else ")")}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(p.seed + 77)
+    for label, per_seq in (("decode_step", p.q_per_seq), ("chunk", 2048)):
+        slots = np.concatenate([wl.positions_to_slots(p, w.block_table, b,
+                                                      np.arange(p.context - per_seq, p.context))
+                                for b in range(p.batch)]).astype(np.int32)
+        kv_new = torch.randn((len(slots), 576), generator=gen, device=dev).to(torch.bfloat16)
+        call = B.prepare_kv_write(kv_new, torch.from_numpy(slots).to(dev), w.pools[0], w.scales[0],
+                                  stream=stream)
+        for _ in range(5):
+            call()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            call()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1000.0 / reps
+        nbytes = len(slots) * per_tok
+        out[label] = {"tokens": int(len(slots)), "us_per_launch": round(us, 2),
+                      "algorithmic_bytes": int(nbytes),
+                      "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    return out
+
+
 def cpu_baseline(w, host, rows, min_seconds=10.0, max_reps=30):
     """Time the CPU oracle on one layer-step (or a row sample of it),
     repeated until about min_seconds of CPU work have run."""
@@ -322,6 +360,9 @@ def main():
         "remap_us_mean": round(statistics.mean(remap_us), 2),
         "roofline": roof,
     }
+    # The KV-cache write runs after the timed decode loop (it overwrites the
+    # last positions of layer 0 of the first table group).
+    result["kv_write"] = measure_kv_write(groups[0], stream, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: copying one layer to the host", file=sys.stderr, flush=True)
         w = groups[0]

@@ -225,6 +225,36 @@ dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_s
                        int64_t rows, int32_t heads, int32_t dv, void* o, float* lse,
                        dcp_out_dtype out_dtype, hipStream_t stream);
 
+/*
+ * Interleaved KV-cache write with FP8 quantisation ([P1] "feat: support
+ * decode context parallelism for PyTorch MLA", File summaries: the KV-cache
+ * fill writes new tokens interleaved over the DCP ranks; [P2] "Feat[DCP]
+ * Support decode context parallelism for DSA models with the flashmla_kv
+ * backend", summary: FP8 caches hold packed FP8, and the review of the
+ * gathered buffer: rows are quantised when written to the persistent cache).
+ *
+ * Token i with slot g = slots[i] >= 0 is written to row g div num_shards of
+ * shard g mod num_shards (interleave 1, the slot naming of dcp_remap_topk).
+ * BF16 pools receive the 576 values unchanged.  FP8 pools receive
+ *   scale = max_d |x[d]| / 448 (fp32 division; 1 for an all-zero token),
+ *   code[d] = E4M3FN(clamp(x[d] / scale, -448, 448)), round to nearest even,
+ * at the shard's row and scale strides.
+ *   kv_new   device bf16 [tokens, 576], 16-byte aligned
+ *   slots    device int32 [tokens]; negative = skip.  Slots must be distinct
+ *            (unchecked: two writes to one row race); a slot whose row is
+ *            beyond its shard's pool_rows is skipped.
+ *   shards   host array of num_shards pools (as for the decode calls; the
+ *            pools are written, local_len is ignored)
+ * Errors (nothing written): DCP_ERR_INVALID_ARGUMENT for tokens < 0, null or
+ * misaligned pointers, num_shards outside 1..16, an unknown dtype or a
+ * shard failing the dcp_kv_shard rules.  tokens == 0 is a no-op.  Ordered
+ * after earlier work on `stream`; a decode reading the same pools must be
+ * ordered after it.
+ */
+dcp_status dcp_kv_write(const void* kv_new, int64_t tokens, const int32_t* slots,
+                        const dcp_kv_shard* shards, int32_t num_shards, dcp_kv_dtype kv_dtype,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

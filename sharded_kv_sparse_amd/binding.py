@@ -27,7 +27,7 @@ OUT_F32, OUT_BF16 = 0, 1
 
 EXPORTS = ("dcp_status_string", "dcp_abi_version", "dcp_remap_topk",
            "dcp_decode_workspace_size", "mla_sparse_decode_lse", "mla_dense_decode_lse",
-           "lse_combine")
+           "lse_combine", "dcp_kv_write")
 
 
 class DcpError(RuntimeError):
@@ -73,6 +73,8 @@ def lib():
     L.mla_dense_decode_lse.restype = ctypes.c_int
     L.lse_combine.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, ctypes.c_int, vp]
     L.lse_combine.restype = ctypes.c_int
+    L.dcp_kv_write.argtypes = [vp, i64, vp, ctypes.POINTER(KvShard), i32, ctypes.c_int, vp]
+    L.dcp_kv_write.restype = ctypes.c_int
     if L.dcp_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.dcp_abi_version()}, the binding "
                            f"expects {ABI_VERSION}: rebuild it")
@@ -312,3 +314,26 @@ def lse_combine(o_part, lse_part, out_dtype=OUT_F32, o=None, lse=None, stream=No
     _check(lib().lse_combine(_ptr(o_part), _ptr(lse_part), n, rows, heads, dv, _ptr(o), _ptr(lse),
                              out_dtype, _stream(o_part.device, stream)), "lse_combine")
     return o, lse
+
+
+# ---------------------------------------------------------------- KV write
+
+def kv_write(kv_new, slots, pools, scales, stream=None):
+    """Write new tokens into the shards' pools in place: kv_new bf16
+    [tokens, 576], slots int32 [tokens] (global slot ids, negative = skip);
+    pools / scales as for the decode calls (FP8 pools are quantised with one
+    fp32 scale per token)."""
+    prepare_kv_write(kv_new, slots, pools, scales, stream)()
+
+
+def prepare_kv_write(kv_new, slots, pools, scales, stream=None):
+    """As kv_write, but returns a PreparedCall instead of calling."""
+    _need(kv_new, torch.bfloat16, "kv_new")
+    if kv_new.dim() != 2 or kv_new.shape[1] != HEAD_DIM:
+        raise ValueError(f"kv_new must be [tokens, {HEAD_DIM}]")
+    _need(slots, torch.int32, "slots", (kv_new.shape[0],))
+    shards, kv_dtype = _shards(pools, scales)
+    args = (_ptr(kv_new), kv_new.shape[0], _ptr(slots), shards, len(pools), kv_dtype,
+            _stream(kv_new.device, stream))
+    return PreparedCall(lib().dcp_kv_write, args, "dcp_kv_write", None, kv_new.device,
+                        (kv_new, slots, pools, scales))

@@ -175,20 +175,24 @@ int merge_wait_ticks() {
   return (int)(v * 100);
 }
 
+// A shard as the kernels see it: strides resolved (0 = packed).
+ShardArg shard_arg(const dcp_kv_shard& s, dcp_kv_dtype kv_dtype) {
+  ShardArg a;
+  a.kv = s.kv;
+  a.scale = s.kv_scale;
+  a.pool_rows = s.pool_rows;
+  a.local_len = s.local_len;
+  a.row_stride = s.row_stride != 0 ? s.row_stride
+                                   : (kv_dtype == DCP_KV_FP8_E4M3 ? kHeadDim : 2 * kHeadDim);
+  a.scale_stride = s.scale_stride != 0 ? s.scale_stride : 4;
+  return a;
+}
+
 DecodeParams make_params(const CommonArgs& a, const WorkspacePlan& w) {
   DecodeParams p;
   std::memset(&p, 0, sizeof(p));
   p.q = a.q;
-  for (int r = 0; r < a.num_shards; ++r) {
-    p.shard[r].kv = a.shards[r].kv;
-    p.shard[r].scale = a.shards[r].kv_scale;
-    p.shard[r].pool_rows = a.shards[r].pool_rows;
-    p.shard[r].row_stride = a.shards[r].row_stride != 0
-                                ? a.shards[r].row_stride
-                                : (a.kv_dtype == DCP_KV_FP8_E4M3 ? kHeadDim : 2 * kHeadDim);
-    p.shard[r].scale_stride = a.shards[r].scale_stride != 0 ? a.shards[r].scale_stride : 4;
-    p.shard[r].local_len = a.shards[r].local_len;
-  }
+  for (int r = 0; r < a.num_shards; ++r) p.shard[r] = shard_arg(a.shards[r], a.kv_dtype);
   p.rows = a.rows;
   p.heads = a.heads;
   p.num_shards = a.num_shards;
@@ -336,6 +340,26 @@ dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_s
   if (rows * heads > 0x7fffffffLL * 4) return DCP_ERR_UNSUPPORTED;
   return launch_combine(o_part, lse_part, num_shards, rows, heads, dv, o, lse,
                         out_dtype == DCP_OUT_BF16, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
+dcp_status dcp_kv_write(const void* kv_new, int64_t tokens, const int32_t* slots,
+                        const dcp_kv_shard* shards, int32_t num_shards, dcp_kv_dtype kv_dtype,
+                        hipStream_t stream) {
+  if (tokens < 0 || num_shards < 1 || num_shards > kMaxShards) return DCP_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != DCP_KV_BF16 && kv_dtype != DCP_KV_FP8_E4M3) return DCP_ERR_INVALID_ARGUMENT;
+  if (tokens == 0) return DCP_OK;
+  if (!kv_new || !slots || reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return DCP_ERR_INVALID_ARGUMENT;
+  dcp_status st = check_shards(shards, num_shards, kv_dtype, false);
+  if (st != DCP_OK) return st;
+  if (tokens > 0x7fffffffLL * 4) return DCP_ERR_UNSUPPORTED;
+  KvWriteParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.kv_new = kv_new;
+  p.slots = slots;
+  p.tokens = tokens;
+  p.num_shards = num_shards;
+  for (int r = 0; r < num_shards; ++r) p.shard[r] = shard_arg(shards[r], kv_dtype);
+  return launch_kv_write(p, kv_dtype == DCP_KV_FP8_E4M3, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -60,6 +60,15 @@ struct DecodeParams {
   int merge_wait_ticks;          // >0: blocks wait up to this many 100 MHz ticks to share a merge
 };
 
+// Arguments of the KV-cache write kernel.
+struct KvWriteParams {
+  const void* kv_new;            // bf16 [tokens, 576]
+  const int* slots;              // [tokens] global slot ids, < 0: skipped
+  long long tokens;
+  int num_shards;
+  ShardArg shard[kMaxShards];
+};
+
 // Workspace plan shared by the size query and the decode calls.
 struct WorkspacePlan {
   int splits;
@@ -82,5 +91,6 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int num_sh
                           int out_bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, bool dense, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, hipStream_t stream);
 
 }  // namespace dcp

@@ -123,6 +123,22 @@ def test_kv_layout_checks(L):
     assert _sparse(L, shards=sh(scale=None, row_stride=640)) == INVALID
 
 
+def test_kv_write_argument_checks(L):
+    def kw(kv_new=0x50000, tokens=4, slots=FAKE, shards=None, n=2, kv=B.KV_FP8_E4M3):
+        return L.dcp_kv_write(kv_new, tokens, slots, _shards(2, fp8=True) if shards is None else shards,
+                              n, kv, None)
+    assert kw(tokens=0, kv_new=None, slots=None) == OK                # no-op
+    assert kw(tokens=-1) == INVALID
+    assert kw(kv_new=None) == INVALID
+    assert kw(kv_new=0x50008) == INVALID                              # not 16-byte aligned
+    assert kw(slots=None) == INVALID
+    assert kw(n=0) == INVALID
+    assert kw(n=17) == INVALID
+    assert kw(kv=7) == INVALID
+    assert kw(shards=_shards(2, fp8=False)) == INVALID                # FP8 needs scales
+    assert kw(shards=_shards(2, fp8=True, pool_rows=0)) == INVALID
+
+
 def test_dense_decode_argument_checks(L):
     def dense(**kw):
         a = dict(q=FAKE, rows=2, heads=64, shards=_shards(2, dense=True), n=2, kv=B.KV_BF16,

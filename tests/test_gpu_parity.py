@@ -380,3 +380,101 @@ def test_inline_scale_workload_layout(gpu):
     res = gpu_sparse(w)
     torch.cuda.synchronize()
     check_against_oracle(res, oracle_sparse(w), "inline scale")
+
+
+# ---------------------------------------------------------------- KV write
+
+def _kv_write_case(gpu, n, kv, rows, tokens, seed, row_bytes=0):
+    rng = np.random.default_rng(seed)
+    pools, scales = [], []
+    for r in range(n):
+        if kv == "bf16":
+            pools.append(torch.randn((rows, 576), device=gpu).to(torch.bfloat16))
+            scales.append(None)
+        elif row_bytes:
+            buf = torch.randint(0, 0x7F, (rows, row_bytes), dtype=torch.uint8, device=gpu)
+            sc = buf.view(torch.float32)[:, 144]
+            sc.copy_(torch.rand(rows, device=gpu) + 0.5)
+            pools.append(buf[:, :576])
+            scales.append(sc)
+        else:
+            pools.append(torch.randint(0, 0x7F, (rows, 576), dtype=torch.uint8, device=gpu))
+            scales.append(torch.rand(rows, device=gpu) + 0.5)
+    slots = rng.choice(n * rows, size=tokens, replace=False).astype(np.int32)
+    slots[rng.random(tokens) < 0.1] = -1                   # skipped tokens
+    slots[0] = n * rows + 3                               # beyond every pool: skipped
+    mag = np.exp2(rng.uniform(-8, 8, size=(tokens, 1)))
+    x = rng.normal(0, 1, size=(tokens, 576)) * mag
+    x[1] = 0.0                                            # an all-zero token
+    x[2, :] = 0.0
+    x[2, 7] = -3.0e-3                                     # one value: codes 0 except +-448
+    kv_new = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(gpu)
+    host_p = [p.cpu().contiguous() for p in pools]
+    host_p = [p.view(torch.int16).numpy().view(np.uint16) if kv == "bf16" else p.numpy() for p in host_p]
+    host_s = [None if s is None else s.cpu().contiguous().numpy() for s in scales]
+    bits = kv_new.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref_p, ref_s = oracle.kv_write(bits, np.where(slots >= n * rows, -1, slots), n, host_p, host_s, kv)
+    say(f"kv write n={n} {kv} rows={rows} tokens={tokens} row_bytes={row_bytes}")
+    B.kv_write(kv_new, torch.from_numpy(slots).to(gpu), pools, scales)
+    torch.cuda.synchronize()
+    for r in range(n):
+        got = pools[r].cpu().contiguous()
+        got = got.view(torch.int16).numpy().view(np.uint16) if kv == "bf16" else got.numpy()
+        np.testing.assert_array_equal(got, ref_p[r])
+        if kv == "fp8":
+            np.testing.assert_array_equal(scales[r].cpu().numpy().view(np.uint32),
+                                          ref_s[r].view(np.uint32))
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+@pytest.mark.parametrize("kv,row_bytes", [("fp8", 0), ("fp8", 640), ("bf16", 0)])
+def test_kv_write_bit_exact(gpu, n, kv, row_bytes):
+    # every pool byte and every scale bit equal to the oracle's, skipped and
+    # out-of-pool slots leave the pools untouched
+    _kv_write_case(gpu, n, kv, rows=700, tokens=900 if n > 1 else 500, seed=40 + n,
+                   row_bytes=row_bytes)
+
+
+def test_kv_write_headline_shape(gpu):
+    # one new token per row of the 64-row FP8 workload, into its 4 pools of
+    # 2M rows: the written rows equal the oracle's quantisation, sampled other
+    # rows are untouched, and the sparse decode of a table that selects the new
+    # tokens matches the oracle on the written values
+    p = wl.preset("sparse_fp8_b64_k2048")
+    w = make(p)
+    n, rows = p.num_shards, p.pool_rows
+    rng = np.random.default_rng(7)
+    pos = p.context - 1
+    slots = np.array([wl.positions_to_slots(p, w.block_table, b, np.array([pos]))[0]
+                      for b in range(p.batch)], dtype=np.int32)
+    kv_new = (torch.randn((p.batch, 576), device=gpu) * 2.0).to(torch.bfloat16)
+    sample = rng.integers(0, rows, 256)
+    before = [(w.pools[0][r][sample].cpu(), w.scales[0][r][sample].cpu()) for r in range(n)]
+    say("kv write headline shape")
+    B.kv_write(kv_new, torch.from_numpy(slots).to(gpu), w.pools[0], w.scales[0])
+    torch.cuda.synchronize()
+    bits = kv_new.cpu().view(torch.int16).numpy().view(np.uint16)
+    touched = set()
+    for i, g in enumerate(slots):
+        r, row = int(g) % n, int(g) // n
+        touched.add((r, row))
+        codes, sc = oracle.quantize_row_e4m3(bits[i])
+        np.testing.assert_array_equal(w.pools[0][r][row].cpu().numpy(), codes)
+        assert w.scales[0][r][row].item() == float(sc)
+    for r in range(n):
+        keep = np.array([(r, int(s)) not in touched for s in sample])
+        np.testing.assert_array_equal(w.pools[0][r][sample].cpu().numpy()[keep], before[r][0].numpy()[keep])
+        np.testing.assert_array_equal(w.scales[0][r][sample].cpu().numpy()[keep], before[r][1].numpy()[keep])
+    # the decode reads what was written: each row's new slot joins its table
+    # (in column 0 unless the row already selects it), and the oracle sees
+    # the new scales
+    table = w.table.copy()
+    for b in range(p.batch):
+        if slots[b] not in table[b]:
+            table[b, 0] = slots[b]
+    w.table = table
+    for r in range(n):
+        w.scales_host[0][r] = w.scales[0][r].cpu().numpy()
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    check_against_oracle(res, oracle_sparse(w), "decode after kv write")
