@@ -305,10 +305,12 @@ def unsharded_dense(q, pools, kv_dtype, scales, block_table, local_lens, page_si
 # and the review of the gathered buffer (rows are quantised when they are
 # written to the persistent cache).  The pages do not give the scale rule;
 # the reading taken here: one fp32 scale per token, the largest magnitude of
-# its 576 values divided by 448 (the largest E4M3FN value), computed in fp32
-# as the kernel does, and 1 for an all-zero token; code = E4M3FN of
-# x / scale rounded to nearest even, in fp32 (a quantised code is an integer
-# decided by floating point, so both sides decide it in the same precision).
+# its 576 values divided by 448 (the largest E4M3FN value), and 1 for an
+# all-zero token; code = E4M3FN of x times the inverse scale 448 / amax,
+# rounded to nearest even.  Every step is one fp32 operation, as in the
+# kernel (a quantised code is an integer decided by floating point, so both
+# sides decide it in the same precision): the scale and the inverse scale are
+# fp32 divisions, x times the inverse scale an fp32 product.
 
 E4M3_MAX = 448.0
 
@@ -341,13 +343,16 @@ def encode_e4m3fn(values):
 
 def quantize_row_e4m3(x_bits):
     """One token's 576 bfloat16 values (bit patterns) -> (codes uint8 [576],
-    scale float32): scale = amax / 448 in fp32 (1 when amax is 0), code =
-    E4M3FN(x / scale) with the fp32 quotient clamped to +-448."""
+    scale float32): scale = amax / 448 and inv = 448 / amax, each one fp32
+    division (both 1 when amax is 0); code = E4M3FN(x * inv), the fp32
+    product clamped to +-448."""
     x = decode_bf16(x_bits).astype(np.float32)        # exact: a bf16 fits in fp32
     amax = np.float32(np.max(np.abs(x)))
-    scale = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
-    q = (x / scale).astype(np.float32)                # IEEE fp32 division per element
-    q = np.clip(q, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    e4m3_max = np.float32(E4M3_MAX)
+    scale = np.float32(amax / e4m3_max) if amax > 0 else np.float32(1.0)
+    inv = np.float32(e4m3_max / amax) if amax > 0 else np.float32(1.0)
+    q = (x * inv).astype(np.float32)                  # one fp32 product per element
+    q = np.clip(q, -e4m3_max, e4m3_max)
     return encode_e4m3fn(q), scale
 
 

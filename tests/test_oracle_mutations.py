@@ -41,8 +41,8 @@ MUTATIONS = [
     ("E4M3 encode truncates", "m8 = np.rint((2.0 * mant - 1.0) * 8.0)", "m8 = np.floor((2.0 * mant - 1.0) * 8.0)"),
     ("E4M3 encode no carry", "carry = m8 == 8", "carry = m8 == 9"),
     ("E4M3 encode subnormal step", "np.rint(a[sub] * 2.0 ** 9)", "np.rint(a[sub] * 2.0 ** 8)"),
-    ("quant scale inverted", "scale = np.float32(amax / np.float32(E4M3_MAX))",
-     "scale = np.float32(np.float32(E4M3_MAX) / amax)"),
+    ("quant scale inverted", "scale = np.float32(amax / e4m3_max)", "scale = np.float32(e4m3_max / amax)"),
+    ("quant divides by the inverse", "q = (x * inv).astype(np.float32)", "q = (x / inv).astype(np.float32)"),
     ("kv write shard by div", "r, row = int(g % num_shards), int(g // num_shards)",
      "r, row = int(g // num_shards) % num_shards, int(g % num_shards)"),
     ("kv write keeps skipped", "        if g < 0:\n            continue\n        r, row",
