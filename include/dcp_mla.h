@@ -236,8 +236,10 @@ dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_s
  * Token i with slot g = slots[i] >= 0 is written to row g div num_shards of
  * shard g mod num_shards (interleave 1, the slot naming of dcp_remap_topk).
  * BF16 pools receive the 576 values unchanged.  FP8 pools receive
- *   scale = max_d |x[d]| / 448 (fp32 division; 1 for an all-zero token),
- *   code[d] = E4M3FN(clamp(x[d] / scale, -448, 448)), round to nearest even,
+ *   scale = amax / 448 and inv = 448 / amax, amax = max_d |x[d]| (fp32
+ *   divisions; both 1 for an all-zero token),
+ *   code[d] = E4M3FN(clamp(x[d] * inv, -448, 448)) (fp32 product), round to
+ *   nearest even,
  * at the shard's row and scale strides.
  *   kv_new   device bf16 [tokens, 576], 16-byte aligned
  *   slots    device int32 [tokens]; negative = skip.  Slots must be distinct

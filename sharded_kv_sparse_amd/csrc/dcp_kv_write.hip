@@ -9,9 +9,10 @@
 // and the review of the gathered buffer (rows are quantised when written to
 // the persistent cache).  Slot g of the DCP-wide pool is row g div N of shard
 // g mod N (interleave 1).  The pages give no scale rule; the one used: scale =
-// (largest |x| of the token's 576 values) / 448, or 1 for an all-zero token,
-// and code = E4M3FN(x / scale), round to nearest even, the fp32 quotient
-// clamped to +-448.  Both divisions are IEEE fp32 divisions.
+// amax / 448 with amax the largest |x| of the token's 576 values, inverse
+// scale 448 / amax (both 1 for an all-zero token), and code = E4M3FN(x *
+// inverse scale), round to nearest even, the fp32 product clamped to +-448.
+// The two divisions are IEEE fp32 divisions, once per token.
 //
 // One wave per token: lane l holds latent values 8l .. 8l + 7 (16 bytes of
 // the bf16 row), lanes 0..7 also RoPE values 512 + 8l .. + 7; the largest
@@ -60,10 +61,11 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(KvWriteParams p
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
     const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 1.0f;
     auto code8 = [&](int base) -> uint2 {
       float q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(__fdiv_rn(x[base + i], scale), -448.0f), 448.0f);
+      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(x[base + i] * inv, -448.0f), 448.0f);
       int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
       lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
       int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
