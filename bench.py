@@ -127,7 +127,7 @@ def flops(p, tokens):
 
 def measure_kv_write(w, stream, dev, reps=50):
     """Time dcp_kv_write on layer 0 of group w: the new tokens of one decode
-    step (q_per_seq per sequence) and a 2048-token chunk per sequence, both
+    step (q_per_seq per sequence) and a chunk of up to 2048 tokens per sequence, both
     at the sequences' last positions; K launches back to back between two
     events on the launch stream.  Algorithmic bytes per token: the bf16 row
     read (1152), its slot (4) and the row written (580 FP8 with its scale,
@@ -138,7 +138,8 @@ def measure_kv_write(w, stream, dev, reps=50):
                      + (", E4M3FN quantisation)" if p.kv_dtype == "fp8" else ")")}
     gen = torch.Generator(device=dev)
     gen.manual_seed(p.seed + 77)
-    for label, per_seq in (("decode_step", p.q_per_seq), ("chunk", 2048)):
+    for label, per_seq in (("decode_step", min(p.q_per_seq, p.context)),
+                           ("chunk", min(2048, p.context))):
         slots = np.concatenate([wl.positions_to_slots(p, w.block_table, b,
                                                       np.arange(p.context - per_seq, p.context))
                                 for b in range(p.batch)]).astype(np.int32)
