@@ -32,6 +32,8 @@
 // arrival and completion words, so the workspace needs zeroing only once.
 #pragma once
 
+#include <type_traits>
+
 #include "dcp_device.h"
 #include "dcp_internal.h"
 
@@ -45,19 +47,37 @@ constexpr int kMaxWaitMembers = 24;         // abandon bits 8..31 of the arrival
 // partial's power of two 2^wx[i][hl], so that the stored values need no
 // rescaling.  Whole block; leaves w in LDS.
 template <int NT>
-__device__ inline void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
+__device__ __forceinline__ void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
                                               bool write_lse, DCP_LDS float* w, DCP_LDS int* wx);
 template <int NT>
-__device__ inline void merge_weights(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
+__device__ __forceinline__ void merge_weights(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
                                      float* out_lse, bool write_lse, DCP_LDS float* w,
                                      DCP_LDS int* wx) {
   const int H = p.heads, tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(p.ws_lse + part0 * H, (unsigned)(n_in * H) * 4u);
   const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(p.ws_exp + part0 * H, wx ? (unsigned)(n_in * H) * 4u : 0u);
-  for (int i = tid; i < n_in * nh; i += NT) {
-    const int pi = i / nh, hl = i - pi * nh;
-    w[pi * kHeadsPerBlock + hl] = load_coherent(rl, (unsigned)(pi * H + h0 + hl) * 4u);
-    if (wx) wx[pi * kHeadsPerBlock + hl] = __float_as_int(load_coherent(rx, (unsigned)(pi * H + h0 + hl) * 4u));
+  // All loads of a round are issued before any is used: one memory round
+  // trip per round instead of one per value.
+  constexpr int R = 8;                        // values per thread per round
+  constexpr unsigned kNowhere = 0x80000000u;  // beyond every resource: reads 0, no traffic
+  for (int base = 0; base < n_in * nh; base += NT * R) {
+    float lv[R];
+    int xv[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = base + k * NT + tid, pi = i / nh, hl = i - pi * nh;
+      const unsigned off = i < n_in * nh ? (unsigned)(pi * H + h0 + hl) * 4u : kNowhere;
+      lv[k] = load_coherent(rl, off);
+      xv[k] = wx ? __float_as_int(load_coherent(rx, off)) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = base + k * NT + tid, pi = i / nh, hl = i - pi * nh;
+      if (i < n_in * nh) {
+        w[pi * kHeadsPerBlock + hl] = lv[k];
+        if (wx) wx[pi * kHeadsPerBlock + hl] = xv[k];
+      }
+    }
   }
   merge_weights_from_lds<NT>(n_in, h0, nh, out_lse, write_lse, w, wx);
 }
@@ -65,7 +85,7 @@ __device__ inline void merge_weights(const DecodeParams& p, long long part0, int
 // The second half of merge_weights: w[i][hl] holds the LSEs (and wx[i][hl]
 // the powers of two of fp16 partials).
 template <int NT>
-__device__ inline void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
+__device__ __forceinline__ void merge_weights_from_lds(int n_in, int h0, int nh, float* out_lse,
                                               bool write_lse, DCP_LDS float* w, DCP_LDS int* wx) {
   const int tid = threadIdx.x;
   __syncthreads();
@@ -110,10 +130,10 @@ struct WsPartials {
 // elements (element e: dim tile e / 4nh, head (e / 4) % nh, lane group e % 4)
 // over the partials part0 .. part0 + n_in - 1 into out (the output row's
 // [H][512] values, fp32 or bf16).  Whole block.
-template <int NT, bool HALF>
-__device__ inline void merge_part(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
-                                  int part, int n_parts, const DCP_LDS float* w, void* out,
-                                  int out_bf16) {
+template <int NT, bool HALF, int K, int G>
+__device__ __forceinline__ void merge_part_kg(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
+                                     int part, int n_parts, const DCP_LDS float* w, void* out,
+                                     int out_bf16) {
   const int tid = threadIdx.x;
   const int T = 128 * nh;
   const int e0 = (int)((long long)part * T / n_parts), e1 = (int)((long long)(part + 1) * T / n_parts);
@@ -121,7 +141,6 @@ __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_
   const unsigned part_bytes = ws.part_bytes;
   const unsigned blk_off = (unsigned)h0 * 128u * ws.kElem;
   constexpr unsigned kNowhere = 0x80000000u;      // beyond every resource: reads 0, no traffic
-  constexpr int K = 8;                             // elements per thread per pass
   for (int eb = e0; eb < e1; eb += NT * K) {
     f32x4 acc[K];
     int hl[K];
@@ -131,22 +150,29 @@ __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_
       const int e = min(eb + k * NT + tid, e1 - 1);
       hl[k] = (e >> 2) % nh;
     }
-    for (int i0 = 0; i0 < n_in; i0 += 4) {
-      f32x4 v[4][K];
+    for (int i0 = 0; i0 < n_in; i0 += G) {
+      // raw loads (packed fp16 stay packed until used)
+      typedef typename std::conditional<HALF, u32x2, f32x4>::type Raw;
+      Raw v[G][K];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < G; ++u)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           const int e = eb + k * NT + tid;
           const bool live = i0 + u < n_in && e < e1;
-          v[u][k] = ws.load(live ? (unsigned)(i0 + u) * part_bytes + blk_off + ws.kElem * e : kNowhere);
+          const unsigned off = live ? (unsigned)(i0 + u) * part_bytes + blk_off + ws.kElem * e : kNowhere;
+          if constexpr (HALF) v[u][k] = load_coherent2(ws.r, off);
+          else v[u][k] = load_coherent4(ws.r, off);
         }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < G; ++u)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           const float wt = i0 + u < n_in ? w[(i0 + u) * kHeadsPerBlock + hl[k]] : 0.f;
-          acc[k] += (wt != 0.f) ? wt * v[u][k] : f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 x;
+          if constexpr (HALF) x = unpack_f16x4(v[u][k]);
+          else x = v[u][k];
+          acc[k] += (wt != 0.f) ? wt * x : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
 #pragma unroll
@@ -166,6 +192,29 @@ __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_
   }
 }
 
+// merge_part_kg with more of a pass's loads in flight when there are many
+// members: up to 16 members, 2 elements per thread and 16 members' loads
+// together; beyond, 1 element and 32 members (one memory round trip per
+// pass while they cover n_in).  A function of its own, so that its loads'
+// registers do not add to the calling kernel's.
+template <int NT, bool HALF>
+__device__ __attribute__((noinline)) void merge_part_many(const DecodeParams& p, long long part0,
+                                                          int n_in, int h0, int nh, int part,
+                                                          int n_parts, const DCP_LDS float* w,
+                                                          void* out, int out_bf16) {
+  if (n_in <= 16) merge_part_kg<NT, HALF, 2, 16>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
+  else merge_part_kg<NT, HALF, 1, 32>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
+}
+
+// Up to 4 members: 8 elements per thread, the members' loads together.
+template <int NT, bool HALF>
+__device__ __forceinline__ void merge_part(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
+                                  int part, int n_parts, const DCP_LDS float* w, void* out,
+                                  int out_bf16) {
+  if (n_in <= 4) merge_part_kg<NT, HALF, 8, 4>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
+  else merge_part_many<NT, HALF>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
+}
+
 // Merges this block's own part (member `member` of NIN = 4 or 8: dim tiles
 // [d0, d0 + 32 / NIN) of every head of the block, d0 = member * 32 / NIN)
 // with its own normalised values own[j] (dim tile d0 + j) taken from
@@ -175,7 +224,7 @@ __device__ inline void merge_part(const DecodeParams& p, long long part0, int n_
 // they are in flight.  Partials are added in index order with the same
 // arithmetic as merge_part, so the result is bit-identical.
 template <int NT, int NIN, bool HALF>
-__device__ inline void merge_own_part(const DecodeParams& p, long long part0, int member, int h0,
+__device__ __forceinline__ void merge_own_part(const DecodeParams& p, long long part0, int member, int h0,
                                       int nh, int hl, int g, const f32x4 (&own)[8],
                                       DCP_LDS float* w, DCP_LDS int* wx, float* out_lse,
                                       bool write_lse, void* out, int out_bf16) {
@@ -304,7 +353,7 @@ struct WsPartial {
 // from the values); pre_stored: the caller already stored the non-own dim
 // tiles of its workspace partial (with that exponent).
 template <int NT, bool OWN = false>
-__device__ inline void finish_block(const DecodeParams& p, long long row, int shard, int split,
+__device__ __forceinline__ void finish_block(const DecodeParams& p, long long row, int shard, int split,
                                     int head, int g, bool writer, const f32x4 (&oacc)[32],
                                     float m_run, float l_tot, DCP_LDS char* smem, int* s_flag,
                                     int ex_given = kExFromValues, bool pre_stored = false) {
