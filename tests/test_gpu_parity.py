@@ -478,3 +478,24 @@ def test_kv_write_headline_shape(gpu):
     res = gpu_sparse(w)
     torch.cuda.synchronize()
     check_against_oracle(res, oracle_sparse(w), "decode after kv write")
+
+
+def test_kv_write_hand_worked_example(gpu):
+    # the kernel's codes and scale equal the ones derived by hand in
+    # tests/golden/kv_write_worked_example.json (exact products, ties to even,
+    # subnormals), written to slot 5 of a 2-shard FP8 pool (shard 1, row 2)
+    import json
+    import os
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_write_worked_example.json")))
+    x = torch.zeros((1, 576), dtype=torch.float32)
+    x[0, :len(ex["values"])] = torch.tensor(ex["values"])
+    pools = [torch.full((4, 576), 0x55, dtype=torch.uint8, device=gpu) for _ in range(2)]
+    scales = [torch.ones(4, dtype=torch.float32, device=gpu) for _ in range(2)]
+    say("kv write hand-worked example")
+    B.kv_write(x.to(torch.bfloat16).to(gpu), torch.tensor([5], dtype=torch.int32, device=gpu), pools, scales)
+    torch.cuda.synchronize()
+    row = pools[1][2].cpu().numpy()
+    np.testing.assert_array_equal(row[:len(ex["codes"])], np.array(ex["codes"], dtype=np.uint8))
+    assert (row[len(ex["codes"]):] == ex["rest_code"]).all()
+    assert format(int(scales[1][2].cpu().numpy().view(np.uint32)), "08x") == ex["scale_bits_hex"]
+    assert (pools[0].cpu().numpy() == 0x55).all() and (pools[1][[0, 1, 3]].cpu().numpy() == 0x55).all()

@@ -116,3 +116,19 @@ def test_kv_write_places_every_slot_by_brute_force(n, kv):
                 np.testing.assert_array_equal(out_p[r][row], pools[r][row])
                 if kv == "fp8":
                     assert out_s[r][row] == scales[r][row]
+
+
+def test_quantize_matches_hand_worked_example():
+    # tests/golden/kv_write_worked_example.json: codes derived by hand from the
+    # E4M3FN bit definition (exact products, two ties to even, subnormals)
+    import json
+    import os
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_write_worked_example.json")))
+    x = np.zeros(576, dtype=np.float32)
+    x[:len(ex["values"])] = ex["values"]
+    bits = bf16_bits(x)
+    assert (oracle.decode_bf16(bits)[:len(ex["values"])] == np.array(ex["values"])).all()  # exact in bf16
+    codes, scale = oracle.quantize_row_e4m3(bits)
+    assert format(int(np.float32(scale).view(np.uint32)), "08x") == ex["scale_bits_hex"]
+    np.testing.assert_array_equal(codes[:len(ex["codes"])], np.array(ex["codes"], dtype=np.uint8))
+    assert (codes[len(ex["codes"]):] == ex["rest_code"]).all()
