@@ -147,6 +147,21 @@ def test_sparse_decode_splits(gpu, kv, splits):
     check_against_oracle(res, oracle_sparse(w), f"splits={splits}")
 
 
+@pytest.mark.parametrize("kv,splits", [("fp8", 8), ("fp8", 12), ("fp8", 32), ("bf16", 32)])
+def test_sparse_decode_many_partials(gpu, kv, splits):
+    # 16, 24 or 64 partials per row (2 shards x splits): the merge's wide load
+    # groups (16 or 32 members per pass, several groups), two rounds of LSE
+    # loads, rows merged by their last block alone (more than 24 partials),
+    # and empty splits; merged and per-shard outputs within tolerance
+    p = wl.Preset("t", "sparse", kv, batch=2, q_per_seq=1, heads=64, context=40000, num_shards=2,
+                  topk=8000, pad_tail=300, seed=60 + splits)
+    w = make(p)
+    say(f"sparse {kv} splits={splits} ({2 * splits} partials per row)")
+    res = gpu_sparse(w, num_splits=splits)
+    torch.cuda.synchronize()
+    check_against_oracle(res, oracle_sparse(w), f"{kv} splits={splits}")
+
+
 @pytest.mark.parametrize("kv,heads", [("fp8", 64), ("fp8", 128), ("bf16", 64), ("bf16", 32)])
 def test_sparse_decode_short_rows(gpu, kv, heads):
     """Rows with 1..16 selected slots and many heads (a case another stack's
