@@ -108,6 +108,15 @@ void decode_fp8_kernel(const DecodeParams p) {
   const int start = split == 0 ? 0 : min(n_tok, split * chunk);
   const int end = min(n_tok, start + chunk);
   const int ntiles = (end - start + kT - 1) / kT;
+  // When the tokens leave a remainder of 1..64 past whole tiles, that short
+  // tile goes first ("lead"): its compute then overlaps the prologue's wait
+  // for the first full tile's rows instead of lengthening the block's end,
+  // which the row's merge waits for.  Tile it covers [tb(it), te(it)).
+  const int rem = (end - start) % kT;
+  const int lead = (ntiles > 1 && rem > 0 && rem <= 64) ? rem : 0;
+  const int shift = lead > 0 ? kT - lead : 0;
+  auto tb = [&](int it) { return start + it * kT - (it > 0 ? shift : 0); };
+  auto te = [&](int it) { return (it == 0 && lead > 0) ? start + lead : min(end, tb(it) + kT); };
 
   // Where the id of local token j lives: the compacted slot id (sparse) or
   // the page id of its logical page (dense).
@@ -129,7 +138,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   // Tokens past the tile's valid count copy the tile's first token: they are
   // masked out of the softmax, and a real row keeps their V codes finite
   // (P' = 0 times a NaN code would still be NaN).
-  auto eff = [&](int it, int t) { return t < min(kT, end - (start + it * kT)) ? t : 0; };
+  auto eff = [&](int it, int t) { return t < te(it) - tb(it) ? t : 0; };
   // A tile's copies are issued in pieces (copy c = 0..17: granule c / 2 of
   // token group 2w + (c & 1), granule-major) so that they can be spread over
   // the MFMA work of the previous tile and the next tile's first k-steps can
@@ -147,7 +156,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   const int chunk_off1 = 16 * ((lane & 3) ^ chunk_sw(dma_tok + 16));
   auto plan_rows = [&](int it, const TileIds& id) {
     RowCopies rc;
-    const int tok0 = start + it * kT;
+    const int tok0 = tb(it);
     rc.prow[0] = pool_row(tok0 + eff(it, dma_tok), id.id[0]);
     rc.prow[1] = pool_row(tok0 + eff(it, dma_tok + 16), id.id[1]);
     rc.prow_sc = pool_row(tok0 + eff(it, sc_tok), id.sc);
@@ -173,7 +182,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   // Ids of tile `it` into ring slot `slot` (waves 2 and 3, 64 tokens each).
   auto issue_ring_slot = [&](int it, int slot) {
     const int t = (wave - 2) * 64 + lane;
-    dma4(id_ptr(start + it * kT + eff(it, t)), ring + slot * kT + (wave - 2) * 64);
+    dma4(id_ptr(tb(it) + eff(it, t)), ring + slot * kT + (wave - 2) * 64);
   };
 
   // ---- tile 0's ids go into ring slot 0 by DMA (waves 2 and 3, like every
@@ -216,7 +225,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   // first, as at the top of every tile, then all its copies.
   const bool issue0 = ntiles > 0, ring1 = ntiles > 1;
   {
-    auto valid0 = [&](int t) { return start + t < end; };
+    auto valid0 = [&](int t) { return start + t < te(0); };
 #pragma unroll
     for (int h = 0; h < 2; ++h) ids0.id[h] = valid0(dma_tok + 16 * h) ? ids0.id[h] : id_first;
     ids0.sc = valid0(sc_tok) ? ids0.sc : id_first;
@@ -362,8 +371,9 @@ void decode_fp8_kernel(const DecodeParams p) {
   // The last tile, when at most 64 of its tokens are valid ("short"),
   // skips the QK pass over S tiles 4..7 and packs the three P' terms of its
   // 64 tokens into the k slots of two MFMAs per dim tile instead of three.
-  auto tile = [&](auto next_c, int it) {
+  auto tile = [&](auto next_c, auto first_c, int it) {
     constexpr bool next = decltype(next_c)::value;
+    constexpr bool first_short = decltype(first_c)::value;   // the short lead tile
     constexpr int NS = 8, NQ = 4, NH = 2;
     wait_vmcnt<10>();
     lds_barrier();                       // granules 0..3 of tile it, its scales, ring(it + 1)
@@ -385,8 +395,9 @@ void decode_fp8_kernel(const DecodeParams p) {
       }
     };
     const DCP_LDS char* sb = smem + (it & 1) * kStageBytes;
-    const int tok0 = start + it * kT;
-    const bool short_tile = !next && end - tok0 <= 64;
+    const int tok0 = tb(it);
+    const int tend = te(it);
+    const bool short_tile = first_short || (!next && tend - tok0 <= 64);
 
     // ---- S^T = K Q^T (base-2 logits), eight 16-token S tiles in two passes of four
     f32x4 sacc[NS];
@@ -396,6 +407,10 @@ void decode_fp8_kernel(const DecodeParams p) {
       if (half == 1 && short_tile) {       // S tiles 4..7 are all masked
 #pragma unroll
         for (int q = 0; q < NQ; ++q) sacc[4 + q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (next) {              // the copies pass 1 would have carried
+#pragma unroll
+          for (int j = 5; j < 9; ++j) issue_copy(rc, it + 1, j);
+        }
         break;
       }
       f32x4 acc[NQ];
@@ -490,7 +505,7 @@ void decode_fp8_kernel(const DecodeParams p) {
     // The token scales are read from LDS twice rather than kept in registers.
     float z[NS][4];
     float tmax = kNegInf;
-    const bool full = tok0 + kT <= end;
+    const bool full = tok0 + kT <= tend;
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
@@ -503,7 +518,7 @@ void decode_fp8_kernel(const DecodeParams p) {
       for (int st = 0; st < NS; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (tok0 + 16 * st + 4 * g + i >= end) z[st][i] = kNegInf;
+          if (tok0 + 16 * st + 4 * g + i >= tend) z[st][i] = kNegInf;
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
@@ -635,13 +650,14 @@ void decode_fp8_kernel(const DecodeParams p) {
       }
       if constexpr (!next) store_pair(15);
     };
-    if (next || !short_tile) pv(BoolC<false>{});
+    if (!short_tile) pv(BoolC<false>{});
     else pv(BoolC<true>{});
   };
   // Tile 0's copies are waited for at its top like any tile's.
   int it = 0;
-  for (; it + 1 < ntiles; ++it) tile(BoolC<true>{}, it);
-  if (it < ntiles) tile(BoolC<false>{}, it);
+  if (lead > 0) tile(BoolC<true>{}, BoolC<true>{}, it++);   // (lead > 0 implies ntiles > 1)
+  for (; it + 1 < ntiles; ++it) tile(BoolC<true>{}, BoolC<false>{}, it);
+  if (it < ntiles) tile(BoolC<false>{}, BoolC<false>{}, it);
   wait_vmcnt<0>();   // copies queued for tiles that turned out empty
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
