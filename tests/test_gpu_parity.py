@@ -514,3 +514,34 @@ def test_kv_write_hand_worked_example(gpu):
     assert (row[len(ex["codes"]):] == ex["rest_code"]).all()
     assert format(int(scales[1][2].cpu().numpy().view(np.uint32)), "08x") == ex["scale_bits_hex"]
     assert (pools[0].cpu().numpy() == 0x55).all() and (pools[1][[0, 1, 3]].cpu().numpy() == 0x55).all()
+
+
+@pytest.mark.parametrize("kind,heads,splits", [("sparse", 64, 0), ("sparse", 128, 0), ("sparse", 64, 2),
+                                               ("dense", 64, 0), ("dense", 128, 0)])
+def test_fp8_lead_short_tile(gpu, kind, heads, splits):
+    # rows whose token counts leave 1..64 tokens past whole 128-token tiles
+    # (the short tile then runs first), with 64 / 65 / whole-tile boundaries
+    lens = [129, 150, 192, 193, 256, 257, 320, 321, 449, 512]
+    if kind == "sparse":
+        p = wl.Preset("t", "sparse", "fp8", batch=len(lens), q_per_seq=1, heads=heads, context=4000,
+                      num_shards=1, topk=max(lens), seed=71 + heads)
+        w = make(p)
+        table = w.table.copy()
+        for i, n in enumerate(lens):
+            table[i, n:] = -1
+        w.table = table
+        say(f"fp8 lead tile sparse H={heads} splits={splits}")
+        res = gpu_sparse(w, num_splits=splits)
+        torch.cuda.synchronize()
+        ref = oracle_sparse(w)
+        np.testing.assert_array_equal(res["counts"].cpu().numpy()[0], np.array(lens))
+    else:
+        p = wl.Preset("t", "dense", "fp8", batch=len(lens), q_per_seq=1, heads=heads, context=1024,
+                      num_shards=1, seed=73 + heads)
+        w = make(p)
+        w.local_lens = np.array([lens], dtype=np.int32)
+        say(f"fp8 lead tile dense H={heads}")
+        res = gpu_dense(w, num_splits=splits)
+        torch.cuda.synchronize()
+        ref = oracle_dense(w)
+    check_against_oracle(res, ref, f"lead tile {kind} H={heads}")
