@@ -11,7 +11,9 @@ a layer between its uses: the KV is read from HBM.
 
 Output: one JSON line (rank 0), plus a roofline figure for the decode kernel
 (algorithmic bytes per launch / average launch time from HIP events recorded
-on the launch stream) and the CPU fp64 oracle timed on the host as a baseline.
+on the launch stream), the interleaved FP8 KV-cache write timed after the
+decode loop (one decode step of new tokens, and a chunk of up to 2048 tokens
+per sequence), and the CPU fp64 oracle timed on the host as a baseline.
 """
 
 import argparse
