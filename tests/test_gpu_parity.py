@@ -545,3 +545,19 @@ def test_fp8_lead_short_tile(gpu, kind, heads, splits):
         torch.cuda.synchronize()
         ref = oracle_dense(w)
     check_against_oracle(res, ref, f"lead tile {kind} H={heads}")
+
+
+@pytest.mark.parametrize("kv,heads,n", [("fp8", 64, 16), ("fp8", 128, 16), ("bf16", 64, 16),
+                                        ("fp8", 32, 16), ("fp8", 64, 1), ("bf16", 16, 1)])
+def test_sparse_decode_shard_count_extremes(gpu, kv, heads, n):
+    # the largest shard count the library takes (16: 16 partials per row, the
+    # own-part merge off) and a single shard (the merge is the identity)
+    p = wl.Preset("t", "sparse", kv, batch=3, q_per_seq=1, heads=heads, context=20000,
+                  num_shards=n, topk=1500, pad_tail=30, seed=80 + n + heads)
+    w = make(p)
+    say(f"sparse {kv} H={heads} N={n}")
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    ref = oracle_sparse(w)
+    np.testing.assert_array_equal(res["counts"].cpu().numpy(), ref["counts"])
+    check_against_oracle(res, ref, f"{kv} H={heads} N={n}")
