@@ -245,8 +245,11 @@ dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_s
  *   slots    device int32 [tokens]; negative = skip.  Slots must be distinct
  *            (unchecked: two writes to one row race); a slot whose row is
  *            beyond its shard's pool_rows is skipped.
- *   shards   host array of num_shards pools (as for the decode calls; the
- *            pools are written, local_len is ignored)
+ *   shards   host array of num_shards pools (as for the decode calls;
+ *            local_len is ignored).  This call writes the rows and scales
+ *            that dcp_kv_shard's kv and kv_scale point to: the struct
+ *            declares them const for the decode calls, which only read
+ *            them, so the caller must pass writable device memory here.
  * Errors (nothing written): DCP_ERR_INVALID_ARGUMENT for tokens < 0, null or
  * misaligned pointers, num_shards outside 1..16, an unknown dtype or a
  * shard failing the dcp_kv_shard rules.  tokens == 0 is a no-op.  Ordered
