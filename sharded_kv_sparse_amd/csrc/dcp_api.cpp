@@ -25,13 +25,13 @@ long long min_splits_for_list(long long tokens_max, bool dense, int page_size) {
   return ceil_div(tokens_max, cap);
 }
 
-dcp_status resolve_splits(long long rows, int num_shards, long long tok_expected,
+dcp_status resolve_splits(long long rows, int num_shards, int heads, long long tok_expected,
                           long long tok_max, bool dense, int page_size, int requested,
                           int* splits_out) {
   if (requested < 0) return DCP_ERR_INVALID_ARGUMENT;
   long long need = min_splits_for_list(tok_max, dense, page_size);
   long long s = requested > 0 ? requested
-                              : std::max<long long>(need, default_splits(rows, num_shards,
+                              : std::max<long long>(need, default_splits(rows, num_shards, heads,
                                                                         tok_expected, tok_max));
   if (s < need) return DCP_ERR_UNSUPPORTED;
   if (s * num_shards > kMaxMergeInputs) return DCP_ERR_UNSUPPORTED;
@@ -41,23 +41,28 @@ dcp_status resolve_splits(long long rows, int num_shards, long long tok_expected
 
 // Sparse: a shard holds about k / N of a row's k slots (at most k).
 // Dense: a shard holds up to max_local_len tokens of a sequence.
-dcp_status plan_splits(bool dense, long long rows, int num_shards, long long tokens_per_shard,
-                       int page_size, int requested, int* splits_out) {
+dcp_status plan_splits(bool dense, long long rows, int num_shards, int heads,
+                       long long tokens_per_shard, int page_size, int requested, int* splits_out) {
   long long expected = dense ? tokens_per_shard : ceil_div(tokens_per_shard, num_shards);
-  return resolve_splits(rows, num_shards, expected, tokens_per_shard, dense, page_size, requested,
-                        splits_out);
+  return resolve_splits(rows, num_shards, heads, expected, tokens_per_shard, dense, page_size,
+                        requested, splits_out);
 }
 
 }  // namespace
 
 // Token splits per (row, shard): enough blocks to cover the chip once, at
-// least 128 tokens per split, at most 32K tokens per split.
-int default_splits(long long rows, int num_shards, long long tok_expected, long long tok_max) {
+// least one tile of tokens per split (128 for 64 or 128 heads, the FP8
+// kernel's tile; 64 for 16 or 32 heads, whose kernel uses 32- or 64-token
+// tiles), at most 32K tokens per split.  Depends on the heads, not the KV
+// dtype, so the workspace size query plans the same splits as the call.
+int default_splits(long long rows, int num_shards, int heads, long long tok_expected,
+                   long long tok_max) {
   (void)tok_max;
+  const long long min_tok = heads <= 32 ? 64 : 128;
   long long units = std::max<long long>(1, rows * num_shards);
   long long s = ceil_div(kAssumedCUs, units);
   s = std::max(s, ceil_div(std::max<long long>(tok_expected, 1), 32768));
-  s = std::min(s, std::max<long long>(1, ceil_div(std::max<long long>(tok_expected, 1), 128)));
+  s = std::min(s, std::max<long long>(1, ceil_div(std::max<long long>(tok_expected, 1), min_tok)));
   s = std::min<long long>(s, kMaxMergeInputs / num_shards);
   return (int)std::max<long long>(1, s);
 }
@@ -269,7 +274,7 @@ size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
   if (!want_partials && !want_merged) return bad;
   if (rows == 0) return 0;
   int splits = 0;
-  if (plan_splits(dense != 0, rows, num_shards, tokens_per_shard, page_size, num_splits, &splits) != DCP_OK)
+  if (plan_splits(dense != 0, rows, num_shards, heads, tokens_per_shard, page_size, num_splits, &splits) != DCP_OK)
     return bad;
   return plan_workspace(rows, heads, num_shards, splits, want_partials != 0, want_merged != 0).total;
 }
@@ -290,7 +295,7 @@ dcp_status mla_sparse_decode_lse(const void* q, int64_t rows, int32_t heads,
   if (rows == 0) return DCP_OK;
   if (!counts || (k > 0 && !topk_local)) return DCP_ERR_INVALID_ARGUMENT;
   int splits = 0;
-  st = plan_splits(false, rows, num_shards, k, 1, num_splits, &splits);
+  st = plan_splits(false, rows, num_shards, heads, k, 1, num_splits, &splits);
   if (st != DCP_OK) return st;
   WorkspacePlan w = plan_workspace(rows, heads, num_shards, splits, o_part != nullptr, o != nullptr);
   if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return DCP_ERR_WORKSPACE_TOO_SMALL;
@@ -319,7 +324,7 @@ dcp_status mla_dense_decode_lse(const void* q, int64_t rows, int32_t heads,
   if (rows == 0) return DCP_OK;
   if (!block_table) return DCP_ERR_INVALID_ARGUMENT;
   int splits = 0;
-  st = plan_splits(true, rows, num_shards, max_local_len, page_size, num_splits, &splits);
+  st = plan_splits(true, rows, num_shards, heads, max_local_len, page_size, num_splits, &splits);
   if (st != DCP_OK) return st;
   WorkspacePlan w = plan_workspace(rows, heads, num_shards, splits, o_part != nullptr, o != nullptr);
   if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return DCP_ERR_WORKSPACE_TOO_SMALL;

@@ -78,7 +78,7 @@ struct WorkspacePlan {
   size_t cnt_row_off, cnt_shard_off, ws_o_off, ws_lse_off, ws_exp_off, total;
 };
 
-int default_splits(long long rows, int num_shards, long long tokens_per_shard_expected,
+int default_splits(long long rows, int num_shards, int heads, long long tokens_per_shard_expected,
                    long long tokens_per_shard_max);
 WorkspacePlan plan_workspace(long long rows, int heads, int num_shards, int splits,
                              bool want_partials, bool want_merged);
