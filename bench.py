@@ -87,6 +87,12 @@ def parse():
     ap.add_argument("--groups", type=int, default=4, help="table groups (4 layers each) rotated")
     ap.add_argument("--layers-per-table", type=int, default=4)
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--launch", choices=["graph", "stream"], default="graph",
+                    help="graph: each step's launches captured once in a HIP graph and replayed "
+                         "(decode steps run under graphs on the pages' systems); stream: every "
+                         "launch issued from the host")
+    ap.add_argument("--min-warmup-s", type=float, default=2.0,
+                    help="keep warming up (whole steps) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the CPU-baseline sample (0 = all rows of one layer-step)")
@@ -193,13 +199,26 @@ def cpu_baseline(w, host, rows, min_seconds=10.0, max_reps=30):
         oracle.lse_merge(np.stack([a for a, _ in parts]), np.stack([b for _, b in parts]))
         times.append(time.perf_counter() - t0)
     t = statistics.median(times) * (p.rows / len(sel))
-    import platform
     return {"value": round(t * 1e6, 1), "unit": "us/layer-step", "cores": int(cores),
             "kind": "oracle",
             "sample": (f"{'all' if len(sel) == p.rows else len(sel)} of {p.rows} rows of one "
                        f"layer-step (remap + {p.num_shards} shard attentions + merge, fp64 numpy), "
                        f"median of {len(times)} runs ({time.perf_counter() - t_all:.1f} s of CPU work), "
-                       f"scaled to {p.rows} rows; host {platform.processor() or 'cpu'}")}
+                       f"scaled to {p.rows} rows; host CPU {cpu_model()}, "
+                       f"{len(os.sched_getaffinity(0))} cores available")}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -261,24 +280,70 @@ def main():
                                                stream=stream) for li in range(lpt)]
         prep.append(d)
 
-    def step(gi, ev=None):
+    def step(gi, ev=None, cap_stream=None):
         d = prep[gi]
         if sparse:
             if ev is not None:
                 ev["remap"][0].record(stream)
-            d["remap"]()
+            d["remap"](cap_stream)
             if ev is not None:
                 ev["remap"][1].record(stream)
         for li in range(lpt):
             if ev is not None:
                 ev["dec"][li][0].record(stream)
-            d["dec"][li]()
+            d["dec"][li](cap_stream)
             if ev is not None:
                 ev["dec"][li][1].record(stream)
 
-    for s in range(args.warmup):
-        step(s % args.groups)
+    # HIP graphs: one per table group, each holding one step's launches (the
+    # remap and the decodes of the layers sharing the table).  The library
+    # queues only kernels (no memsets, no allocation), so a replay is the
+    # same work as the eager step; the first replays are checked against the
+    # eager result below.
+    graphs = None
+    if args.launch == "graph":
+        eager = []
+        for gi in range(args.groups):
+            step(gi)
+            torch.cuda.synchronize()
+            eager.append((o.clone(), lse.clone()))
+        graphs = []
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for gi in range(args.groups):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    step(gi, cap_stream=cap)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            for gi in range(args.groups):
+                o.zero_()
+                lse.zero_()
+                torch.cuda.synchronize()
+                graphs[gi].replay()
+                torch.cuda.synchronize()
+                if not (torch.equal(o, eager[gi][0]) and torch.equal(lse, eager[gi][1])):
+                    print(f"[bench] graph replay {rep} of group {gi} differs from the eager step",
+                          file=sys.stderr)
+                    sys.exit(3)
+
+    def run_step(s):
+        if graphs is not None:
+            graphs[s % args.groups].replay()
+        else:
+            step(s % args.groups)
+
+    t_w = time.perf_counter()
+    s = 0
+    while s < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
+        run_step(s)
+        s += 1
+        if s % args.groups == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_steps = s
 
     def mk():
         return torch.cuda.Event(enable_timing=True)
@@ -291,7 +356,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(args.steps):
-        step(s % args.groups)
+        run_step(s)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -343,6 +408,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "launch": ("one HIP graph per step (remap + the layers' decodes), replayed"
+                   if graphs is not None else "kernels launched from the host"),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": False,
         "scaling": "weak",

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DCP_ABI_VERSION 2
+#define DCP_ABI_VERSION 3
 #define DCP_HEAD_DIM 576
 #define DCP_V_DIM 512
 #define DCP_MAX_SHARDS 16
@@ -101,6 +101,15 @@ const char* dcp_status_string(dcp_status status);
 int32_t dcp_abi_version(void);
 
 /*
+ * Process-wide bound, in microseconds (0..100000), of how long the blocks of
+ * a row wait for each other to share the fused merge of the decode calls (see
+ * dcp_decode_workspace_size).  Takes effect for calls queued after it; the
+ * results are bit-identical for every value.  DCP_ERR_INVALID_ARGUMENT out of
+ * range.
+ */
+dcp_status dcp_set_merge_wait_us(int32_t us);
+
+/*
  * Step 1 -- index remap ([P3] Modifications, Index remap; remapped tables are
  * reused by the layers that share a top-k, [P3] Modifications, Decode latency).
  *
@@ -136,11 +145,12 @@ dcp_status dcp_remap_topk(const int32_t* topk_global, int64_t rows, int32_t k,
  * Calls that share one workspace must be ordered on one stream.
  *
  * Merge scheduling.  When the whole grid of a call fits on the device at
- * once, the blocks of a row wait for each other (for at most
- * DCP_MERGE_WAIT_US microseconds, read from the environment at every call;
- * default 30, 0 = never wait) so that each merges a share of the row; a
- * block that stops waiting hands its share to the block that arrives last.
- * The result is bit-identical either way.
+ * once, the blocks of a row wait for each other (for at most the merge wait
+ * set by dcp_set_merge_wait_us, else DCP_MERGE_WAIT_US microseconds read from
+ * the environment once, at the first decode call; default 30, 0 = never
+ * wait) so that each merges a share of the row; a block that stops waiting
+ * hands its share to the block that arrives last.  The result is
+ * bit-identical either way.
  */
 size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
                                  int32_t num_shards, int64_t tokens_per_shard,
@@ -174,6 +184,7 @@ size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
  *                and fp32 [rows, heads]: the merged result
  *   At least one of the pairs (o_part, lse_part) / (o, lse) must be given,
  *   each pair complete.
+ *   softmax_scale  finite and > 0 (else DCP_ERR_INVALID_ARGUMENT)
  *   num_splits   token splits per (row, shard); 0 = library default
  *   workspace    device, >= dcp_decode_workspace_size(...) bytes (may be NULL
  *                when that size is 0)

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdcpmla.so")
 
-ABI_VERSION = 2           # DCP_ABI_VERSION this binding's structures follow
+ABI_VERSION = 3           # DCP_ABI_VERSION this binding's structures follow
 HEAD_DIM = 576
 V_DIM = 512
 MAX_SHARDS = 16
@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "DCP_OK", 1: "DCP_ERR_INVALID_ARGUMENT", 2: "DCP_ERR_UNSUPPOR
 KV_BF16, KV_FP8_E4M3 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 
-EXPORTS = ("dcp_status_string", "dcp_abi_version", "dcp_remap_topk",
+EXPORTS = ("dcp_status_string", "dcp_abi_version", "dcp_set_merge_wait_us", "dcp_remap_topk",
            "dcp_decode_workspace_size", "mla_sparse_decode_lse", "mla_dense_decode_lse",
            "lse_combine", "dcp_kv_write")
 
@@ -59,6 +59,8 @@ def lib():
     L.dcp_status_string.restype = ctypes.c_char_p
     L.dcp_abi_version.argtypes = []
     L.dcp_abi_version.restype = i32
+    L.dcp_set_merge_wait_us.argtypes = [i32]
+    L.dcp_set_merge_wait_us.restype = ctypes.c_int
     L.dcp_remap_topk.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
     L.dcp_remap_topk.restype = ctypes.c_int
     L.dcp_decode_workspace_size.argtypes = [i32, i64, i32, i32, i64, i32, i32, i32, i32]
@@ -116,6 +118,12 @@ def _kv_dtype(pool):
     if pool.dtype == torch.uint8:
         return KV_FP8_E4M3
     raise TypeError("KV pools are bfloat16 rows or uint8 E4M3FN codes")
+
+
+def set_merge_wait_us(us):
+    """Bound (microseconds) of the wait of a row's blocks for each other in
+    the fused merge; process-wide, results bit-identical for every value."""
+    _check(lib().dcp_set_merge_wait_us(int(us)), "dcp_set_merge_wait_us")
 
 
 # ---------------------------------------------------------------- step 1

@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument checks, split and workspace planning, and
 // dispatch to the HIP kernels.  Every check runs before anything is queued, so
 // a rejected call writes nothing.  No allocation, no synchronisation.
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -139,7 +140,7 @@ dcp_status check_common(const CommonArgs& a, bool dense) {
   if (a.rows < 0 || a.num_shards < 1 || a.num_shards > kMaxShards) return DCP_ERR_INVALID_ARGUMENT;
   if (a.kv_dtype != DCP_KV_BF16 && a.kv_dtype != DCP_KV_FP8_E4M3) return DCP_ERR_INVALID_ARGUMENT;
   if (a.out_dtype != DCP_OUT_F32 && a.out_dtype != DCP_OUT_BF16) return DCP_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(a.softmax_scale)) return DCP_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(a.softmax_scale) || !(a.softmax_scale > 0.f)) return DCP_ERR_INVALID_ARGUMENT;
   if (a.heads < 1 || a.num_splits < 0) return DCP_ERR_INVALID_ARGUMENT;
   if ((a.o_part == nullptr) != (a.lse_part == nullptr)) return DCP_ERR_INVALID_ARGUMENT;
   if ((a.o == nullptr) != (a.lse == nullptr)) return DCP_ERR_INVALID_ARGUMENT;
@@ -167,17 +168,33 @@ long long device_cus() {
 }
 
 // Bound of the wait for the other blocks of a row before merging, in
-// 100 MHz ticks: DCP_MERGE_WAIT_US microseconds (default 30; 0 disables
-// waiting, so the last block to arrive merges the whole row).
-int merge_wait_ticks() {
+// microseconds (0 disables waiting, so the last block to arrive merges the
+// whole row).  Starts from DCP_MERGE_WAIT_US, read from the environment once
+// at the first decode call (default 30); dcp_set_merge_wait_us changes it.
+constexpr int kMergeWaitUnset = -1;
+std::atomic<int> g_merge_wait_us{kMergeWaitUnset};
+
+int merge_wait_us_from_env() {
   const char* e = std::getenv("DCP_MERGE_WAIT_US");
   long v = 30;
   if (e && *e) {
     char* end = nullptr;
     const long x = std::strtol(e, &end, 10);
-    if (end != e && x >= 0 && x <= 100000) v = x;
+    if (end != e && x >= 0 && x <= kMaxMergeWaitUs) v = x;
   }
-  return (int)(v * 100);
+  return (int)v;
+}
+
+// The bound in 100 MHz ticks (the kernels' s_memrealtime clock).
+int merge_wait_ticks() {
+  int v = g_merge_wait_us.load(std::memory_order_relaxed);
+  if (v == kMergeWaitUnset) {
+    int expect = kMergeWaitUnset;
+    g_merge_wait_us.compare_exchange_strong(expect, merge_wait_us_from_env(),
+                                            std::memory_order_relaxed);
+    v = g_merge_wait_us.load(std::memory_order_relaxed);
+  }
+  return v * 100;
 }
 
 // A shard as the kernels see it: strides resolved (0 = packed).
@@ -250,6 +267,12 @@ const char* dcp_status_string(dcp_status status) {
 }
 
 int32_t dcp_abi_version(void) { return DCP_ABI_VERSION; }
+
+dcp_status dcp_set_merge_wait_us(int32_t us) {
+  if (us < 0 || us > kMaxMergeWaitUs) return DCP_ERR_INVALID_ARGUMENT;
+  g_merge_wait_us.store(us, std::memory_order_relaxed);
+  return DCP_OK;
+}
 
 dcp_status dcp_remap_topk(const int32_t* topk_global, int64_t rows, int32_t k,
                           int32_t num_shards, int32_t shard, int32_t* topk_local,

@@ -245,6 +245,12 @@ void decode_kernel(const DecodeParams p) {
   f32x4 oacc[32];
 #pragma unroll
   for (int d = 0; d < 32; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // FP8: P' = p * scale goes to fp16 times 2^pe_run, one power of two per
+  // head that puts the head's largest P' so far in [2^14, 2^15): no overflow
+  // whatever the token scales, and O^T carries the same factor until the end
+  // of the tile loop.  kNoExp: no P' above zero seen yet.
+  constexpr int kNoExp = 1000;
+  [[maybe_unused]] int pe_run = kNoExp;
 
   for (int it = 0; it < kStages - 1 && it < ntiles; ++it) issue_tile(it);
 
@@ -421,9 +427,31 @@ void decode_kernel(const DecodeParams p) {
       // V^T operands are read in groups of 8 (FP8) / 4 (BF16) 16-dim tiles,
       // one group ahead of the MFMAs that consume them.
       if constexpr (FP8) {
-        const f16x8 bp = f16x8{(_Float16)pr[0][0], (_Float16)pr[0][1], (_Float16)pr[0][2],
-                               (_Float16)pr[0][3], (_Float16)pr[1][0], (_Float16)pr[1][1],
-                               (_Float16)pr[1][2], (_Float16)pr[1][3]};
+        // The head's largest P' over its four lanes sets the power of two; a
+        // larger P' than before lowers it, and O^T is scaled down to match
+        // (an exact power-of-two multiply).
+        float pmax = 0.f;
+#pragma unroll
+        for (int st = 0; st < CST; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pmax = fmaxf(pmax, pr[st][i]);
+        pmax = max_xor32(max_xor16(pmax));
+        if (pmax > 0.f) {
+          const int pe = -half_exponent(pmax);
+          if (pe < pe_run) {
+            if (pe_run != kNoExp) {
+              const float f = pow2i(pe - pe_run);
+#pragma unroll
+              for (int d = 0; d < 32; ++d) oacc[d] *= f;
+            }
+            pe_run = pe;
+          }
+        }
+        const float ps = pe_run != kNoExp ? pow2i(pe_run) : 1.0f;
+        const f16x8 bp = f16x8{(_Float16)(pr[0][0] * ps), (_Float16)(pr[0][1] * ps),
+                               (_Float16)(pr[0][2] * ps), (_Float16)(pr[0][3] * ps),
+                               (_Float16)(pr[1][0] * ps), (_Float16)(pr[1][1] * ps),
+                               (_Float16)(pr[1][2] * ps), (_Float16)(pr[1][3] * ps)};
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           if (grp + 1 < 4) {
@@ -473,6 +501,14 @@ void decode_kernel(const DecodeParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    }
+  }
+
+  if constexpr (FP8) {          // remove the P' power of two from O^T
+    if (pe_run != kNoExp) {
+      const float f = pow2i(-pe_run);
+#pragma unroll
+      for (int d = 0; d < 32; ++d) oacc[d] *= f;
     }
   }
 

@@ -17,6 +17,7 @@ constexpr int kHeadsPerBlock = 64;       // heads one decode block handles
 constexpr int kMaxList = 4096;           // slot ids / pages a decode block stages in LDS
 constexpr int kMaxMergeInputs = 64;      // partials one merge may combine (N * splits)
 constexpr int kAssumedCUs = 256;         // MI355X compute units (split heuristic only)
+constexpr int kMaxMergeWaitUs = 100000;  // upper bound of the merge wait setting
 
 struct ShardArg {
   const void* kv;

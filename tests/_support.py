@@ -6,6 +6,9 @@ KV values): max |dO| <= 1e-2, max |dLSE| <= 1e-3; -inf must match exactly and
 any NaN fails.  Integer outputs (remap) must be bit-exact.
 """
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -118,7 +121,20 @@ def check_against_oracle(res, ref, what, rows=None, heads=None):
         bf16 = res["o"].dtype == torch.bfloat16
         out["merged"] = assert_attn_close(sel(res["o"]), sel(res["lse"]), ref["o"], ref["lse"],
                                           f"{what} merged", o_rel=2.0 ** -8 if bf16 else 0.0)
+    record_margins(what, out)
     return out
+
+
+def record_margins(what, margins):
+    """Append the measured max |dO| / |dLSE| of a parity case as one JSON line
+    to the file named by DCP_PARITY_MARGINS (nothing when it is unset)."""
+    path = os.environ.get("DCP_PARITY_MARGINS")
+    if not path:
+        return
+    with open(path, "a") as f:
+        for part, (d_o, d_lse) in margins.items():
+            f.write(json.dumps({"case": what, "output": part, "max_abs_dO": d_o,
+                                "max_abs_dLSE": d_lse, "tol_O": O_TOL, "tol_LSE": LSE_TOL}) + "\n")
 
 
 def make(p, device="cuda", layers=1):

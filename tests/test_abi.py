@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.dcp_abi_version() == 2
+    assert L.dcp_abi_version() == B.ABI_VERSION == 3
     for code, name in B.STATUS_NAMES.items():
         assert L.dcp_status_string(code).decode() == name
     assert L.dcp_status_string(99).decode() == "DCP_ERR_UNKNOWN"
@@ -95,6 +95,8 @@ def test_sparse_decode_argument_checks(L):
     assert _sparse(L, o_part=FAKE) == INVALID
     assert _sparse(L, scale=float("nan")) == INVALID
     assert _sparse(L, scale=float("inf")) == INVALID
+    assert _sparse(L, scale=0.0) == INVALID                        # the softmax scale is positive
+    assert _sparse(L, scale=-0.07) == INVALID
     assert _sparse(L, splits=-2) == INVALID
     assert _sparse(L, splits=40) == UNSUPPORTED                    # 2 shards x 40 > 64 partials
     assert _sparse(L, kv=B.KV_FP8_E4M3) == INVALID                 # FP8 needs scales
@@ -156,6 +158,15 @@ def test_dense_decode_argument_checks(L):
     assert dense(max_len=-1) == INVALID
     assert dense(max_len=8 * 64 + 1) == INVALID                    # beyond the block table
     assert dense(heads=24) == UNSUPPORTED
+    assert dense(scale=0.0) == INVALID
+    assert dense(scale=-1.0) == INVALID
+
+
+def test_merge_wait_setting_range(L):
+    assert L.dcp_set_merge_wait_us(-1) == INVALID
+    assert L.dcp_set_merge_wait_us(100001) == INVALID
+    assert L.dcp_set_merge_wait_us(0) == OK
+    assert L.dcp_set_merge_wait_us(30) == OK
 
 
 def test_combine_argument_checks(L):

@@ -51,6 +51,34 @@ def test_remap_bit_exact_small_exhaustive(gpu):
                 np.testing.assert_array_equal(c1.cpu().numpy()[0], ref_counts[s])
 
 
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_remap_bit_exact_multi_segment(gpu, n):
+    # rows wider than one 2048-entry segment: the kept-entry counts of one
+    # segment carry into the next, in order; rows with many, few or no kept
+    # entries, and padding spread through the row
+    rng = np.random.default_rng(40 + n)
+    for k in (2049, 4096, 8000):
+        rows = 6
+        table = np.full((rows, k), -1, dtype=np.int32)
+        for i in range(rows - 1):
+            nv = [k, k - 1, k // 2, 3, 2048][i]
+            vals = rng.choice(50 * k, size=nv, replace=False).astype(np.int32)
+            pos = np.sort(rng.choice(k, size=nv, replace=False))
+            table[i, pos] = vals
+        if n > 1:                      # a row owned entirely by shard n - 1
+            table[1] = (rng.choice(30 * k, size=k, replace=False) * n + (n - 1)).astype(np.int32)
+        say(f"remap multi-segment n={n} k={k}")
+        ref_local, ref_counts = oracle.remap_topk(table, n)
+        local, counts = B.remap_topk(torch.from_numpy(table).to(gpu), n)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(local.cpu().numpy(), ref_local)
+        np.testing.assert_array_equal(counts.cpu().numpy(), ref_counts)
+        s = n - 1
+        l1, c1 = B.remap_topk(torch.from_numpy(table).to(gpu), n, shard=s)
+        np.testing.assert_array_equal(l1.cpu().numpy()[0], ref_local[s])
+        np.testing.assert_array_equal(c1.cpu().numpy()[0], ref_counts[s])
+
+
 @pytest.mark.parametrize("name", ["sparse_bf16_b8_k2048", "sparse_fp8_b64_k2048",
                                   "mtp_sparse_bf16_b16x6_k2048"])
 def test_remap_bit_exact_workload_tables(gpu, name):
@@ -159,7 +187,10 @@ def test_sparse_decode_many_partials(gpu, kv, splits):
     say(f"sparse {kv} splits={splits} ({2 * splits} partials per row)")
     res = gpu_sparse(w, num_splits=splits)
     torch.cuda.synchronize()
-    check_against_oracle(res, oracle_sparse(w), f"{kv} splits={splits}")
+    ref = oracle_sparse(w)
+    np.testing.assert_array_equal(res["local"].cpu().numpy(), ref["local"])    # k = 8000: 4 segments
+    np.testing.assert_array_equal(res["counts"].cpu().numpy(), ref["counts"])
+    check_against_oracle(res, ref, f"{kv} splits={splits}")
 
 
 @pytest.mark.parametrize("kv,heads", [("fp8", 64), ("fp8", 128), ("bf16", 64), ("bf16", 32)])
@@ -186,6 +217,33 @@ def test_sparse_all_empty_rows(gpu):
     torch.cuda.synchronize()
     assert (to_np(res["o"]) == 0).all() and (to_np(res["lse"]) == -np.inf).all()
     assert (to_np(res["o_part"]) == 0).all()
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64])
+def test_fp8_large_token_scales(gpu, heads):
+    # Tokens with scales 2^9 .. 2^12 (and small codes, so their values stay
+    # moderate): P' = p * scale reaches 2^20, beyond fp16, so the 16/32-head
+    # kernel must scale P' per head before converting it; the 64-head kernel
+    # splits P' at a power of two per head.  Partials and the merge within
+    # tolerance of the oracle.
+    p = wl.Preset("t", "sparse", "fp8", batch=3, q_per_seq=1, heads=heads, context=3000,
+                  num_shards=2, topk=300, seed=70 + heads)
+    w = make(p)
+    rng = np.random.default_rng(80 + heads)
+    local, counts = oracle.remap_topk(w.table, p.num_shards, p.pool_rows)
+    for r in range(p.num_shards):
+        used = np.unique(np.concatenate([local[r, i, :counts[r, i]] for i in range(p.rows)]))
+        big = rng.choice(used, size=min(40, used.size), replace=False)
+        idx = torch.from_numpy(big.astype(np.int64)).to(gpu)
+        w.pools[0][r][idx] = w.pools[0][r][idx] & 0x87      # exponent field 0: |code| <= 7 * 2^-9
+        s = w.scales_host[0][r].copy()
+        s[big] = np.exp2(rng.integers(9, 13, size=big.size)).astype(np.float32)
+        w.scales_host[0][r] = s
+        w.scales[0][r].copy_(torch.from_numpy(s).to(gpu))
+    say(f"sparse fp8 large token scales H={heads}")
+    res = gpu_sparse(w)
+    torch.cuda.synchronize()
+    check_against_oracle(res, oracle_sparse(w), f"large scales H={heads}")
 
 
 @pytest.mark.parametrize("name", ["sparse_bf16_b8_k2048", "sparse_fp8_b64_k2048",
@@ -236,7 +294,7 @@ def test_fused_equals_unfused_and_counters_reset(gpu):
 
 
 @pytest.mark.parametrize("name", ["sparse_fp8_b64_k2048", "sparse_bf16_b8_k2048"])
-def test_fused_merge_modes_agree(gpu, name, monkeypatch):
+def test_fused_merge_modes_agree(gpu, name):
     # The row's blocks share the merge (bounded wait), give up at once (1 us),
     # or never wait (the last block merges everything): bit-identical results,
     # counters back at zero every time, and within tolerance of the oracle.
@@ -251,9 +309,12 @@ def test_fused_merge_modes_agree(gpu, name, monkeypatch):
     res = {}
     for us in ["30", "1", "0", "30"]:
         say(f"merge wait {us} us")
-        monkeypatch.setenv("DCP_MERGE_WAIT_US", us)
-        r = B.sparse_decode(w.q, w.pools[0], w.scales[0], local, counts, p.sigma, workspace=ws)
-        torch.cuda.synchronize()
+        B.set_merge_wait_us(int(us))
+        try:
+            r = B.sparse_decode(w.q, w.pools[0], w.scales[0], local, counts, p.sigma, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            B.set_merge_wait_us(30)
         assert (ws[: 8 * p.rows * hb].view(torch.int32) == 0).all()
         if us in res:
             assert torch.equal(r["o"], res[us]["o"]) and torch.equal(r["lse"], res[us]["lse"])
@@ -495,13 +556,17 @@ def test_kv_write_headline_shape(gpu):
     check_against_oracle(res, oracle_sparse(w), "decode after kv write")
 
 
-def test_kv_write_hand_worked_example(gpu):
+@pytest.mark.parametrize("golden", ["kv_write_worked_example.json", "kv_write_product_vs_division.json"])
+def test_kv_write_hand_worked_example(gpu, golden):
     # the kernel's codes and scale equal the ones derived by hand in
-    # tests/golden/kv_write_worked_example.json (exact products, ties to even,
-    # subnormals), written to slot 5 of a 2-shard FP8 pool (shard 1, row 2)
+    # tests/golden (exact products, ties to even, subnormals; a token whose
+    # scale is not a power of two, where the product by the inverse scale is
+    # a tie that dividing by the scale would not give), written to slot 5 of
+    # a 2-shard FP8 pool (shard 1, row 2)
     import json
     import os
-    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_write_worked_example.json")))
+    with open(os.path.join(os.path.dirname(__file__), "golden", golden)) as f:
+        ex = json.load(f)
     x = torch.zeros((1, 576), dtype=torch.float32)
     x[0, :len(ex["values"])] = torch.tensor(ex["values"])
     pools = [torch.full((4, 576), 0x55, dtype=torch.uint8, device=gpu) for _ in range(2)]

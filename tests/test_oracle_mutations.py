@@ -45,6 +45,9 @@ MUTATIONS = [
     ("quant divides by the inverse", "q = (x * inv).astype(np.float32)", "q = (x / inv).astype(np.float32)"),
     ("kv write shard by div", "r, row = int(g % num_shards), int(g // num_shards)",
      "r, row = int(g // num_shards) % num_shards, int(g % num_shards)"),
+    ("quant divides by the scale", "q = (x * inv).astype(np.float32)", "q = (x / scale).astype(np.float32)"),
+    ("kv write placement blocked", "r, row = int(g % num_shards), int(g // num_shards)",
+     "r, row = int(g // pools[0].shape[0]), int(g % pools[0].shape[0])"),
     ("kv write keeps skipped", "        if g < 0:\n            continue\n        r, row",
      "        if g < -1:\n            continue\n        r, row"),
 ]
