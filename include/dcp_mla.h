@@ -50,13 +50,19 @@ extern "C" {
 #define DCP_HEAD_DIM 576
 #define DCP_V_DIM 512
 #define DCP_MAX_SHARDS 16
+/* Static device scratch of mla_sparse_decode_lse_noalloc, per GPU: the
+ * first DCP_NOALLOC_COUNTER_BYTES hold merge counters, the rest partials. */
+#define DCP_NOALLOC_SCRATCH_BYTES (64LL << 20)
+#define DCP_NOALLOC_COUNTER_BYTES (64LL << 10)
 
 typedef enum dcp_status {
   DCP_OK = 0,
   DCP_ERR_INVALID_ARGUMENT = 1,  /* null pointer, non-positive size, bad index   */
   DCP_ERR_UNSUPPORTED = 2,       /* valid but not implemented (e.g. heads = 48)  */
   DCP_ERR_WORKSPACE_TOO_SMALL = 3,
-  DCP_ERR_LAUNCH = 4             /* the HIP runtime rejected a kernel launch     */
+  DCP_ERR_LAUNCH = 4,            /* the HIP runtime rejected a kernel launch     */
+  DCP_ERR_SCRATCH_TOO_SMALL = 5  /* a no-allocation call needs more than the
+                                    library's static scratch                    */
 } dcp_status;
 
 typedef enum dcp_kv_dtype {
@@ -197,6 +203,33 @@ dcp_status mla_sparse_decode_lse(const void* q, int64_t rows, int32_t heads,
                                  dcp_out_dtype out_dtype, int32_t num_splits,
                                  void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/*
+ * mla_sparse_decode_lse without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics and results
+ * as mla_sparse_decode_lse (the same kernels run); the partials and counters
+ * of the fused merge live in a static device array of the library,
+ * DCP_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the first call until
+ * the process ends.  This call allocates and frees nothing.
+ *   - A call whose merge needs more than the scratch (more than
+ *     DCP_NOALLOC_COUNTER_BYTES of counters, or more than the rest for
+ *     partials; e.g. 64 rows x 64 heads x 4 shards needs about 34 MB, 128 such
+ *     rows too much) returns DCP_ERR_SCRATCH_TOO_SMALL before queuing anything.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's partials.  The counters start at zero and every call leaves them
+ *     zero; calls that overlap on one GPU (other streams, other threads, an
+ *     unordered graph) race and give wrong results: order them.
+ *   - The first call on a device looks up the scratch's device address and
+ *     queues a small kernel on `stream` that clears the counters.
+ */
+dcp_status mla_sparse_decode_lse_noalloc(const void* q, int64_t rows, int32_t heads,
+                                         const dcp_kv_shard* shards, int32_t num_shards,
+                                         dcp_kv_dtype kv_dtype, const int32_t* topk_local,
+                                         const int32_t* counts, int32_t k, float softmax_scale,
+                                         float* o_part, float* lse_part, void* o, float* lse,
+                                         dcp_out_dtype out_dtype, int32_t num_splits,
+                                         hipStream_t stream);
 
 /*
  * Step 2 (+ step 3 fused) -- dense absorbed-MLA decode with LSE over every

@@ -21,12 +21,14 @@ MAX_SHARDS = 16
 
 DCP_OK = 0
 STATUS_NAMES = {0: "DCP_OK", 1: "DCP_ERR_INVALID_ARGUMENT", 2: "DCP_ERR_UNSUPPORTED",
-                3: "DCP_ERR_WORKSPACE_TOO_SMALL", 4: "DCP_ERR_LAUNCH"}
+                3: "DCP_ERR_WORKSPACE_TOO_SMALL", 4: "DCP_ERR_LAUNCH",
+                5: "DCP_ERR_SCRATCH_TOO_SMALL"}
 KV_BF16, KV_FP8_E4M3 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 
 EXPORTS = ("dcp_status_string", "dcp_abi_version", "dcp_set_merge_wait_us", "dcp_remap_topk",
-           "dcp_decode_workspace_size", "mla_sparse_decode_lse", "mla_dense_decode_lse",
+           "dcp_decode_workspace_size", "mla_sparse_decode_lse", "mla_sparse_decode_lse_noalloc",
+           "mla_dense_decode_lse",
            "lse_combine", "dcp_kv_write")
 
 
@@ -69,6 +71,10 @@ def lib():
                                         vp, vp, i32, f32, vp, vp, vp, vp, ctypes.c_int, i32,
                                         vp, sz, vp]
     L.mla_sparse_decode_lse.restype = ctypes.c_int
+    L.mla_sparse_decode_lse_noalloc.argtypes = [vp, i64, i32, ctypes.POINTER(KvShard), i32,
+                                                ctypes.c_int, vp, vp, i32, f32, vp, vp, vp, vp,
+                                                ctypes.c_int, i32, vp]
+    L.mla_sparse_decode_lse_noalloc.restype = ctypes.c_int
     L.mla_dense_decode_lse.argtypes = [vp, i64, i32, ctypes.POINTER(KvShard), i32, ctypes.c_int,
                                        vp, i32, i32, i64, f32, vp, vp, vp, vp, ctypes.c_int, i32,
                                        vp, sz, vp]
@@ -267,6 +273,37 @@ def prepare_sparse_decode(q, pools, scales, topk_local, counts, softmax_scale,
     keep = (q, pools, scales, topk_local, counts, workspace)
     return PreparedCall(lib().mla_sparse_decode_lse, args, "mla_sparse_decode_lse", res, q.device,
                         keep)
+
+
+def sparse_decode_noalloc(q, pools, scales, topk_local, counts, softmax_scale,
+                          want_partials=False, want_merged=True, out_dtype=OUT_F32, num_splits=0,
+                          out=None, stream=None):
+    """As sparse_decode, through mla_sparse_decode_lse_noalloc: the fused
+    merge uses the library's static scratch instead of a workspace."""
+    return prepare_sparse_decode_noalloc(q, pools, scales, topk_local, counts, softmax_scale,
+                                         want_partials, want_merged, out_dtype, num_splits, out,
+                                         stream)()
+
+
+def prepare_sparse_decode_noalloc(q, pools, scales, topk_local, counts, softmax_scale,
+                                  want_partials=False, want_merged=True, out_dtype=OUT_F32,
+                                  num_splits=0, out=None, stream=None):
+    """As sparse_decode_noalloc, but returns a PreparedCall instead of calling."""
+    _need(q, torch.bfloat16, "q")
+    rows, heads, _ = q.shape
+    n = len(pools)
+    _need(topk_local, torch.int32, "topk_local")
+    k = topk_local.shape[-1]
+    _need(topk_local, torch.int32, "topk_local", (n, rows, k))
+    _need(counts, torch.int32, "counts", (n, rows))
+    shards, kv_dtype = _shards(pools, scales)
+    res = _outputs(q, n, want_partials, want_merged, out_dtype, out)
+    args = (_ptr(q), rows, heads, shards, n, kv_dtype, _ptr(topk_local), _ptr(counts), k,
+            float(softmax_scale), _ptr(res.get("o_part")), _ptr(res.get("lse_part")),
+            _ptr(res.get("o")), _ptr(res.get("lse")), out_dtype, num_splits,
+            _stream(q.device, stream))
+    return PreparedCall(lib().mla_sparse_decode_lse_noalloc, args, "mla_sparse_decode_lse_noalloc",
+                        res, q.device, (q, pools, scales, topk_local, counts))
 
 
 def dense_decode(q, pools, scales, block_table, local_lens, page_size, max_local_len,

@@ -248,6 +248,50 @@ dcp_status launch_checked(const DecodeParams& p, bool fp8, bool dense, hipStream
   return launch_decode(p, fp8, dense, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
 }
 
+// The sparse decode call, with the caller's workspace or (noalloc) the
+// library's static scratch: counters at its start, partials after
+// kNoallocCounterBytes.
+dcp_status sparse_decode(const CommonArgs& a, const int32_t* topk_local, const int32_t* counts,
+                         int32_t k, bool noalloc, hipStream_t stream) {
+  dcp_status st = check_common(a, false);
+  if (st != DCP_OK) return st;
+  if (k < 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (a.rows == 0) return DCP_OK;
+  if (!counts || (k > 0 && !topk_local)) return DCP_ERR_INVALID_ARGUMENT;
+  int splits = 0;
+  st = plan_splits(false, a.rows, a.num_shards, a.heads, k, 1, a.num_splits, &splits);
+  if (st != DCP_OK) return st;
+  WorkspacePlan w = plan_workspace(a.rows, a.heads, a.num_shards, splits, a.o_part != nullptr,
+                                   a.o != nullptr);
+  DecodeParams p;
+  if (!noalloc) {
+    if (w.total > 0 && (!a.workspace || a.workspace_bytes < w.total))
+      return DCP_ERR_WORKSPACE_TOO_SMALL;
+    p = make_params(a, w);
+  } else {
+    // counters occupy [0, ws_o_off) of the plan, partials [ws_o_off, total)
+    const size_t parts = w.total > w.ws_o_off ? w.total - w.ws_o_off : 0;
+    if (w.total > 0 && (w.ws_o_off > (size_t)kNoallocCounterBytes ||
+                        parts > (size_t)(kNoallocScratchBytes - kNoallocCounterBytes)))
+      return DCP_ERR_SCRATCH_TOO_SMALL;
+    void* base = nullptr;
+    if (w.total > 0 && noalloc_scratch(stream, &base) != hipSuccess) return DCP_ERR_LAUNCH;
+    CommonArgs b = a;
+    b.workspace = base;
+    p = make_params(b, w);
+    if (w.total > 0) {
+      char* part_base = static_cast<char*>(base) + kNoallocCounterBytes;
+      p.ws_o = reinterpret_cast<float*>(part_base);
+      p.ws_lse = reinterpret_cast<float*>(part_base + (w.ws_lse_off - w.ws_o_off));
+      p.ws_exp = reinterpret_cast<int*>(part_base + (w.ws_exp_off - w.ws_o_off));
+    }
+  }
+  p.topk_local = topk_local;
+  p.counts = counts;
+  p.k = k;
+  return launch_checked(p, a.kv_dtype == DCP_KV_FP8_E4M3, false, stream);
+}
+
 }  // namespace
 }  // namespace dcp
 
@@ -262,6 +306,7 @@ const char* dcp_status_string(dcp_status status) {
     case DCP_ERR_UNSUPPORTED: return "DCP_ERR_UNSUPPORTED";
     case DCP_ERR_WORKSPACE_TOO_SMALL: return "DCP_ERR_WORKSPACE_TOO_SMALL";
     case DCP_ERR_LAUNCH: return "DCP_ERR_LAUNCH";
+    case DCP_ERR_SCRATCH_TOO_SMALL: return "DCP_ERR_SCRATCH_TOO_SMALL";
   }
   return "DCP_ERR_UNKNOWN";
 }
@@ -312,21 +357,19 @@ dcp_status mla_sparse_decode_lse(const void* q, int64_t rows, int32_t heads,
                                  hipStream_t stream) {
   CommonArgs a{q, rows, heads, shards, num_shards, kv_dtype, softmax_scale, o_part, lse_part,
                o, lse, out_dtype, num_splits, workspace, workspace_bytes};
-  dcp_status st = check_common(a, false);
-  if (st != DCP_OK) return st;
-  if (k < 0) return DCP_ERR_INVALID_ARGUMENT;
-  if (rows == 0) return DCP_OK;
-  if (!counts || (k > 0 && !topk_local)) return DCP_ERR_INVALID_ARGUMENT;
-  int splits = 0;
-  st = plan_splits(false, rows, num_shards, heads, k, 1, num_splits, &splits);
-  if (st != DCP_OK) return st;
-  WorkspacePlan w = plan_workspace(rows, heads, num_shards, splits, o_part != nullptr, o != nullptr);
-  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return DCP_ERR_WORKSPACE_TOO_SMALL;
-  DecodeParams p = make_params(a, w);
-  p.topk_local = topk_local;
-  p.counts = counts;
-  p.k = k;
-  return launch_checked(p, kv_dtype == DCP_KV_FP8_E4M3, false, stream);
+  return sparse_decode(a, topk_local, counts, k, false, stream);
+}
+
+dcp_status mla_sparse_decode_lse_noalloc(const void* q, int64_t rows, int32_t heads,
+                                         const dcp_kv_shard* shards, int32_t num_shards,
+                                         dcp_kv_dtype kv_dtype, const int32_t* topk_local,
+                                         const int32_t* counts, int32_t k, float softmax_scale,
+                                         float* o_part, float* lse_part, void* o, float* lse,
+                                         dcp_out_dtype out_dtype, int32_t num_splits,
+                                         hipStream_t stream) {
+  CommonArgs a{q, rows, heads, shards, num_shards, kv_dtype, softmax_scale, o_part, lse_part,
+               o, lse, out_dtype, num_splits, nullptr, 0};
+  return sparse_decode(a, topk_local, counts, k, true, stream);
 }
 
 dcp_status mla_dense_decode_lse(const void* q, int64_t rows, int32_t heads,

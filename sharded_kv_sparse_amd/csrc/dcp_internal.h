@@ -18,6 +18,9 @@ constexpr int kMaxList = 4096;           // slot ids / pages a decode block stag
 constexpr int kMaxMergeInputs = 64;      // partials one merge may combine (N * splits)
 constexpr int kAssumedCUs = 256;         // MI355X compute units (split heuristic only)
 constexpr int kMaxMergeWaitUs = 100000;  // upper bound of the merge wait setting
+// Static scratch of mla_sparse_decode_lse_noalloc: counters first, partials after.
+constexpr long long kNoallocScratchBytes = DCP_NOALLOC_SCRATCH_BYTES;
+constexpr long long kNoallocCounterBytes = DCP_NOALLOC_COUNTER_BYTES;
 
 struct ShardArg {
   const void* kv;
@@ -93,5 +96,9 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int num_sh
 hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, bool dense, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, hipStream_t stream);
+
+// Device address of this device's static scratch (looked up, and its counter
+// area cleared on `stream`, at the first call on each device).
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
 
 }  // namespace dcp

@@ -14,7 +14,7 @@ from sharded_kv_sparse_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dcp_mla.h")
 
-OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+OK, INVALID, UNSUPPORTED, WS_SMALL, SCRATCH_SMALL = 0, 1, 2, 3, 5
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
 
 
@@ -104,6 +104,34 @@ def test_sparse_decode_argument_checks(L):
     assert _sparse(L, ws=None, ws_bytes=0) == WS_SMALL             # merged output needs counters
     assert _sparse(L, ws_bytes=16) == WS_SMALL
     assert _sparse(L, rows=0, q=None, shards=None, local=None, counts=None) == OK
+
+
+def _noalloc(L, **kw):
+    a = dict(q=FAKE, rows=4, heads=64, shards=_shards(2), n=2, kv=B.KV_BF16, local=FAKE,
+             counts=FAKE, k=64, scale=0.07, o_part=None, lse_part=None, o=FAKE, lse=FAKE,
+             out=B.OUT_F32, splits=0)
+    a.update(kw)
+    return L.mla_sparse_decode_lse_noalloc(a["q"], a["rows"], a["heads"], a["shards"], a["n"],
+                                           a["kv"], a["local"], a["counts"], a["k"], a["scale"],
+                                           a["o_part"], a["lse_part"], a["o"], a["lse"], a["out"],
+                                           a["splits"], None)
+
+
+def test_noalloc_decode_argument_checks(L):
+    # the same host checks as the workspace entry point, then the scratch limit
+    # (checked before the scratch is touched, so no GPU is needed here)
+    assert _noalloc(L, q=None) == INVALID
+    assert _noalloc(L, heads=48) == UNSUPPORTED
+    assert _noalloc(L, scale=0.0) == INVALID
+    assert _noalloc(L, o=None, lse=None) == INVALID
+    assert _noalloc(L, splits=40) == UNSUPPORTED
+    assert _noalloc(L, rows=0, q=None, shards=None, local=None, counts=None) == OK
+    # 1024 rows x 64 heads x 4 shards: about 537 MB of partials > the 63 MiB of scratch
+    assert _noalloc(L, rows=1024, shards=_shards(4), n=4, k=2048) == SCRATCH_SMALL
+    # 4096 rows x 16 heads, one shard: about 135 MB of partials
+    assert _noalloc(L, rows=4096, heads=16, splits=1, shards=_shards(1), n=1) == SCRATCH_SMALL
+    # per-shard partials of one split use no scratch: nothing to reject
+    assert _noalloc(L, rows=0, o=None, lse=None, o_part=FAKE, lse_part=FAKE) == OK
 
 
 def test_kv_layout_checks(L):
