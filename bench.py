@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--min-warmup-s", type=float, default=2.0,
                     help="keep warming up (whole steps) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill-over-a-cached-prefix timing")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the CPU-baseline sample (0 = all rows of one layer-step)")
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
@@ -170,6 +172,92 @@ def measure_kv_write(w, stream, dev, reps=50):
                       "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     return out
+
+
+def measure_prefill(stream, dev, reps=20, name="prefill_fp8_prefix16k_new2k"):
+    """Time the prefill over a cached prefix on its workload: for every
+    bounded chunk, the gather from the shards (dcp_gather_prefix), the new
+    tokens' attention to the chunk (mla_prefill_chunk_lse) and the running
+    merge (lse_merge_into, fp32 accumulator); each kind of launch timed over
+    `reps` passes by events on the launch stream, and the whole pass.
+    Algorithmic bytes: gather 2 x 580 (FP8) or 2 x 1152 (BF16) per token,
+    merge 3 x (512 x 4 + 4) per (token, head); attention flops 2 x (576 +
+    512) per (token, head, chunk token)."""
+    p = wl.PREFILL_PRESETS[name]
+    pw = wl.make_prefill_workload(p, device=dev)
+    w = pw.cache
+    q = pw.q[0]
+    tokens, heads = p.new_tokens, p.heads
+    chunks = wl.prefix_chunks(p)
+    c_max = max(ln for _, ln in chunks)
+    fp8 = p.kv_dtype == "fp8"
+    kv = torch.empty((c_max, 576), dtype=w.pools[0][0].dtype, device=dev)
+    sc = torch.empty((c_max,), dtype=torch.float32, device=dev) if fp8 else None
+    o_c = torch.empty((tokens, heads, 512), dtype=torch.float32, device=dev)
+    lse_c = torch.empty((tokens, heads), dtype=torch.float32, device=dev)
+    o = torch.zeros((tokens, heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.full((tokens, heads), float("-inf"), dtype=torch.float32, device=dev)
+    ws_n = B.prefill_workspace_size(tokens, heads, c_max)
+    ws = B.alloc_workspace(ws_n, dev) if ws_n else None
+    bt = w.dev(w.block_table[0]).reshape(1, -1)
+    calls = []
+    for beg, ln in chunks:
+        calls.append((
+            B.prepare_gather_prefix(bt, w.pools[0], w.scales[0], p.page_size, [beg], [ln], out_kv=kv[:ln],
+                                    out_scale=sc[:ln] if fp8 else None, stream=stream),
+            B.prepare_prefill_chunk_attention(q, kv[:ln], sc[:ln] if fp8 else None, p.sigma, o_c, lse_c,
+                                              workspace=ws, stream=stream),
+            B.prepare_merge_into(o, lse, o_c, lse_c, stream=stream)))
+
+    def mk():
+        return torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        for c in calls:
+            for f in c:
+                f()
+    torch.cuda.synchronize()
+    ev = [[(mk(), mk()) for _ in range(3)] for _ in range(reps * len(calls))]
+    t0, t1 = mk(), mk()
+    t0.record(stream)
+    for r in range(reps):
+        for c in calls:
+            for f in c:
+                f()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    whole_us = t0.elapsed_time(t1) * 1000.0 / reps
+    i = 0
+    for r in range(reps):
+        for c in calls:
+            for k, f in enumerate(c):
+                ev[i][k][0].record(stream)
+                f()
+                ev[i][k][1].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    per = [statistics.mean(e[k][0].elapsed_time(e[k][1]) * 1000.0 for e in ev) for k in range(3)]
+    mean_chunk = statistics.mean(ln for _, ln in chunks)
+    g_bytes = mean_chunk * (2 * 580 if fp8 else 2 * 1152)
+    a_flops = 2.0 * (576 + 512) * tokens * heads * mean_chunk
+    m_bytes = 3 * tokens * heads * (512 * 4 + 4)
+    peak = FP8_MFMA_PEAK_TFLOPS if fp8 else BF16_MFMA_PEAK_TFLOPS
+    return {
+        "workload": p.name, "note": p.note,
+        "us_per_prefix_pass": round(whole_us, 1),
+        "chunks": len(chunks),
+        "gather": {"kernel": "gather_prefix_kernel", "us_per_chunk": round(per[0], 2),
+                   "gbps": round(g_bytes / (per[0] * 1e-6) / 1e9, 1),
+                   "frac_hbm_peak": round(g_bytes / (per[0] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "attention": {"kernel": ("decode_fp8_kernel<true>" if fp8 and heads * tokens % 64 == 0
+                                 else "decode_kernel") + " (dense, one contiguous chunk)",
+                      "us_per_chunk": round(per[1], 2),
+                      "tflops": round(a_flops / (per[1] * 1e-6) / 1e12, 1),
+                      "frac_mfma_peak": round(a_flops / (per[1] * 1e-6) / 1e12 / peak, 4),
+                      "peak_tflops": peak},
+        "merge": {"kernel": "merge_into_kernel", "us_per_chunk": round(per[2], 2),
+                  "gbps": round(m_bytes / (per[2] * 1e-6) / 1e9, 1),
+                  "frac_hbm_peak": round(m_bytes / (per[2] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
 
 
 def cpu_baseline(w, host, rows, min_seconds=10.0, max_reps=30):
@@ -448,6 +536,10 @@ def main():
     # The KV-cache write runs after the timed decode loop (it overwrites the
     # last positions of layer 0 of the first table group).
     result["kv_write"] = measure_kv_write(groups[0], stream, dev)
+    if not args.no_prefill:
+        del groups, prep
+        torch.cuda.empty_cache()
+        result["prefill_prefix"] = measure_prefill(stream, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: copying one layer to the host", file=sys.stderr, flush=True)
         w = groups[0]

@@ -270,6 +270,74 @@ dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_s
                        dcp_out_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Prefill over a cached prefix, step 1 -- gather ([P1] "feat: support decode
+ * context parallelism for PyTorch MLA", Summary, prefill bullet: the
+ * cached-prefix KV is gathered in bounded chunks; [P2] "Feat[DCP] Support
+ * decode context parallelism for DSA models with the flashmla_kv backend",
+ * summary: with an FP8 cache the gathered buffer keeps the packed FP8 rows,
+ * nothing is dequantised).
+ *
+ * For every sequence b < num_seqs and j < out_offset[b+1] - out_offset[b]:
+ * position t = pos_begin[b] + j, slot g = block_table[b][t div (page*N)] *
+ * page*N + t mod (page*N) (the DCP-wide logical page holds page*N positions),
+ * and row g div N of shard g mod N is copied unchanged to chunk row
+ * out_offset[b] + j (its fp32 scale to out_scale[out_offset[b] + j] for FP8).
+ *   block_table  device int32 [num_seqs, max_pages]
+ *   shards       host array of num_shards pools (local_len ignored)
+ *   pos_begin    device int32 [num_seqs]; out_offset device int32 [num_seqs + 1],
+ *                non-decreasing, out_offset[0] = 0
+ *   max_len      host bound of every out_offset[b+1] - out_offset[b] (sizes the grid)
+ *   out_kv       device [out_offset[num_seqs], 576] E4M3FN codes or bf16, 16-byte aligned
+ *   out_scale    device fp32 [out_offset[num_seqs]] (FP8; may be NULL for BF16)
+ * Positions past the block table or rows past a pool are clamped into range
+ * (unspecified data, nothing read out of bounds).  num_seqs <= 65535.
+ */
+dcp_status dcp_gather_prefix(const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                             const dcp_kv_shard* shards, int32_t num_shards, dcp_kv_dtype kv_dtype,
+                             const int32_t* pos_begin, const int32_t* out_offset, int32_t num_seqs,
+                             int32_t max_len, void* out_kv, float* out_scale, hipStream_t stream);
+
+/* Workspace bytes of mla_prefill_chunk_lse (0 = none; SIZE_MAX for arguments
+ * it would reject).  Zero it once after allocating; calls leave it zeroed. */
+size_t dcp_prefill_workspace_size(int64_t tokens, int32_t heads, int64_t chunk_len);
+
+/*
+ * Prefill, step 2 -- attention of the new tokens to one gathered chunk, with
+ * LSE ([P1] Summary, prefill bullet).  The cached prefix precedes every new
+ * token, so each query row attends every chunk token:
+ *   z_j = softmax_scale * q[t][h] . K[j],  O[t][h] = sum_j e^{z_j} V[j] / sum_j e^{z_j},
+ *   lse[t][h] = ln sum_j e^{z_j};  chunk_len == 0 gives O = 0, lse = -inf.
+ *   q          device bf16 [tokens, heads, 576]; heads in {16, 32, 64, 128}
+ *   chunk_kv   device [chunk_len, 576] E4M3FN codes (value = code * chunk_scale)
+ *              or bf16, packed rows, 16-byte aligned (dcp_gather_prefix output);
+ *              chunk_kv and chunk_scale may be NULL when chunk_len == 0
+ *   o, lse     device fp32 [tokens, heads, 512] and [tokens, heads]
+ * Runs the dense decode kernels with (token, head) rows regrouped 64 heads to
+ * a row, so that a block reads the chunk once for 64 query rows.
+ */
+dcp_status mla_prefill_chunk_lse(const void* q, int64_t tokens, int32_t heads,
+                                 const void* chunk_kv, const float* chunk_scale,
+                                 int64_t chunk_len, dcp_kv_dtype kv_dtype, float softmax_scale,
+                                 float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Prefill, step 3 -- running LSE merge of chunk partials ([P1] review
+ * exchange on prefix_output: fp32 merge arithmetic, the running output stored
+ * in BF16 or kept in fp32).  In place, for every (row, head):
+ *   (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_new, lse_new))
+ * with the merge of lse_combine (a side with LSE = -inf is skipped; both
+ * empty gives O = 0, LSE = -inf).  Start the accumulator at lse = -inf (its O
+ * is then never read) or at the first chunk's result.
+ *   o_acc    device [rows, heads, dv], fp32 or bf16 per acc_dtype
+ *   lse_acc  device fp32 [rows, heads]
+ *   o_new, lse_new  device fp32 [rows, heads, dv], [rows, heads]
+ */
+dcp_status lse_merge_into(void* o_acc, float* lse_acc, const float* o_new, const float* lse_new,
+                          int64_t rows, int32_t heads, int32_t dv, dcp_out_dtype acc_dtype,
+                          hipStream_t stream);
+
+/*
  * Interleaved KV-cache write with FP8 quantisation ([P1] "feat: support
  * decode context parallelism for PyTorch MLA", File summaries: the KV-cache
  * fill writes new tokens interleaved over the DCP ranks; [P2] "Feat[DCP]

@@ -23,4 +23,9 @@ from .dcp_oracle import (  # noqa: F401
     encode_e4m3fn,
     quantize_row_e4m3,
     kv_write,
+    prefix_slot,
+    gather_prefix,
+    prefix_chunk_attention,
+    round_bf16,
+    merge_running,
 )

@@ -382,3 +382,72 @@ def kv_write(kv_new_bits, slots, num_shards, pools, scales, kv_dtype):
             pools[r][row] = codes
             scales[r][row] = sc
     return pools, scales
+
+
+# ---------------------------------------------------------------------------
+# Prefill over a cached prefix: bounded chunks gathered from the shards, one
+# attention per chunk with its LSE, and a running LSE merge of the chunks
+# ([P1] "feat: support decode context parallelism for PyTorch MLA", Summary,
+# prefill bullet: the cached-prefix KV is gathered in bounded chunks; review
+# exchange on prefix_output: merge arithmetic in fp32, the running result
+# stored in BF16.  [P2] "Feat[DCP] Support decode context parallelism for DSA
+# models with the flashmla_kv backend", summary: with an FP8 cache the
+# gathered temporary buffer keeps the cache's packed FP8, no dequantisation.)
+# ---------------------------------------------------------------------------
+
+def prefix_slot(block_table_row, num_shards, page_size, position):
+    """Global slot of a sequence position: the DCP-wide logical page holds
+    page_size * N positions, so position t sits in logical page
+    t div (page_size * N) at offset t mod (page_size * N)."""
+    span = int(page_size) * int(num_shards)
+    t = int(position)
+    return int(block_table_row[t // span]) * span + t % span
+
+
+def gather_prefix(block_table_row, num_shards, page_size, pools, scales, kv_dtype, begin,
+                  length):
+    """Positions begin .. begin + length - 1 of one sequence, gathered from the
+    shards into one contiguous chunk in the cache's own format: the stored
+    rows (bf16 bit patterns or E4M3FN codes) and, for FP8, their scales.
+    Slot g is row g div N of shard g mod N (as for remap_topk)."""
+    n = int(num_shards)
+    rows = np.zeros((int(length), D_K), dtype=np.asarray(pools[0]).dtype)
+    sc = np.zeros(int(length), dtype=np.float32) if kv_dtype == "fp8" else None
+    for j in range(int(length)):
+        g = prefix_slot(block_table_row, n, page_size, int(begin) + j)
+        r, row = g % n, g // n
+        rows[j] = pools[r][row]
+        if sc is not None:
+            sc[j] = scales[r][row]
+    return rows, sc
+
+
+def prefix_chunk_attention(q, chunk_rows, chunk_scales, kv_dtype, sigma):
+    """Every query row of every new token attends every token of the chunk
+    (the cached prefix precedes all new tokens, so nothing is masked).
+    q [T, H, 576] float64 -> (O [T, H, 512], lse [T, H])."""
+    q = np.asarray(q, dtype=np.float64)
+    t, h, _ = q.shape
+    keys = dequant_rows(chunk_rows, np.arange(len(chunk_rows)), kv_dtype, chunk_scales)
+    o, lse = attend(q.reshape(t * h, D_K), keys, sigma)
+    return o.reshape(t, h, D_V), lse.reshape(t, h)
+
+
+def round_bf16(x):
+    """float64 -> the nearest bfloat16 value, ties to even, as float64: a
+    bfloat16 keeps 8 significant bits, so with x = m * 2^e (m in [0.5, 1))
+    the result is rint(m * 2^8) * 2^(e - 8) (exact in float64; values here
+    stay far inside bfloat16's exponent range)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def merge_running(o_acc, lse_acc, o_new, lse_new, store_bf16=False):
+    """One step of the running merge of chunk partials: the LSE merge of the
+    accumulated (O, LSE) and a new chunk's (O, LSE).  store_bf16: the merged O
+    is stored rounded to bfloat16 (the LSE stays fp32)."""
+    o, lse = lse_merge(np.stack([o_acc, o_new]), np.stack([lse_acc, lse_new]))
+    if store_bf16:
+        o = round_bf16(o)
+    return o, lse

@@ -29,7 +29,8 @@ OUT_F32, OUT_BF16 = 0, 1
 EXPORTS = ("dcp_status_string", "dcp_abi_version", "dcp_set_merge_wait_us", "dcp_remap_topk",
            "dcp_decode_workspace_size", "mla_sparse_decode_lse", "mla_sparse_decode_lse_noalloc",
            "mla_dense_decode_lse",
-           "lse_combine", "dcp_kv_write")
+           "lse_combine", "dcp_kv_write", "dcp_gather_prefix", "dcp_prefill_workspace_size",
+           "mla_prefill_chunk_lse", "lse_merge_into")
 
 
 class DcpError(RuntimeError):
@@ -83,6 +84,16 @@ def lib():
     L.lse_combine.restype = ctypes.c_int
     L.dcp_kv_write.argtypes = [vp, i64, vp, ctypes.POINTER(KvShard), i32, ctypes.c_int, vp]
     L.dcp_kv_write.restype = ctypes.c_int
+    L.dcp_gather_prefix.argtypes = [vp, i32, i32, ctypes.POINTER(KvShard), i32, ctypes.c_int, vp, vp,
+                                    i32, i32, vp, vp, vp]
+    L.dcp_gather_prefix.restype = ctypes.c_int
+    L.dcp_prefill_workspace_size.argtypes = [i64, i32, i64]
+    L.dcp_prefill_workspace_size.restype = sz
+    L.mla_prefill_chunk_lse.argtypes = [vp, i64, i32, vp, vp, i64, ctypes.c_int, f32, vp, vp, vp, sz,
+                                        vp]
+    L.mla_prefill_chunk_lse.restype = ctypes.c_int
+    L.lse_merge_into.argtypes = [vp, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
+    L.lse_merge_into.restype = ctypes.c_int
     if L.dcp_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.dcp_abi_version()}, the binding "
                            f"expects {ABI_VERSION}: rebuild it")
@@ -382,3 +393,144 @@ def prepare_kv_write(kv_new, slots, pools, scales, stream=None):
             _stream(kv_new.device, stream))
     return PreparedCall(lib().dcp_kv_write, args, "dcp_kv_write", None, kv_new.device,
                         (kv_new, slots, pools, scales))
+
+
+# ---------------------------------------------------------------- prefill over a cached prefix
+
+def gather_prefix(block_table, pools, scales, page_size, pos_begin, lengths, out_kv=None,
+                  out_scale=None, stream=None):
+    """Gather positions pos_begin[b] .. + lengths[b] of every sequence b from
+    the shards into one chunk buffer (rows of sequence b after those of
+    b - 1), in the cache's own format.  block_table int32 [num_seqs,
+    max_pages] (device); pos_begin, lengths: host sequences of ints.
+    Returns (chunk rows [total, 576], chunk scales [total] or None)."""
+    return prepare_gather_prefix(block_table, pools, scales, page_size, pos_begin, lengths,
+                                 out_kv, out_scale, stream)()
+
+
+def prepare_gather_prefix(block_table, pools, scales, page_size, pos_begin, lengths, out_kv=None,
+                          out_scale=None, stream=None):
+    """As gather_prefix, but returns a PreparedCall instead of calling."""
+    _need(block_table, torch.int32, "block_table")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, max_pages]")
+    num_seqs, max_pages = block_table.shape
+    if len(pos_begin) != num_seqs or len(lengths) != num_seqs:
+        raise ValueError("one pos_begin and one length per sequence")
+    shards, kv_dtype = _shards(pools, scales)
+    dev = block_table.device
+    offs = [0]
+    for n in lengths:
+        offs.append(offs[-1] + int(n))
+    total = offs[-1]
+    pb = torch.tensor([int(x) for x in pos_begin], dtype=torch.int32).to(dev)
+    oo = torch.tensor(offs, dtype=torch.int32).to(dev)
+    if out_kv is None:
+        out_kv = torch.empty((total, HEAD_DIM), dtype=pools[0].dtype, device=dev)
+    _need(out_kv, pools[0].dtype, "out_kv", (total, HEAD_DIM))
+    if kv_dtype == KV_FP8_E4M3 and out_scale is None:
+        out_scale = torch.empty((total,), dtype=torch.float32, device=dev)
+    if out_scale is not None:
+        _need(out_scale, torch.float32, "out_scale", (total,))
+    max_len = max([int(n) for n in lengths] + [0])
+    args = (_ptr(block_table), max_pages, int(page_size), shards, len(pools), kv_dtype, _ptr(pb),
+            _ptr(oo), num_seqs, max_len, _ptr(out_kv), _ptr(out_scale), _stream(dev, stream))
+    return PreparedCall(lib().dcp_gather_prefix, args, "dcp_gather_prefix", (out_kv, out_scale), dev,
+                        (block_table, pools, scales, pb, oo))
+
+
+def prefill_workspace_size(tokens, heads, chunk_len):
+    n = lib().dcp_prefill_workspace_size(tokens, heads, chunk_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise DcpError(1, "dcp_prefill_workspace_size")
+    return n
+
+
+def prefill_chunk_attention(q, chunk_kv, chunk_scale, softmax_scale, o=None, lse=None,
+                            workspace=None, stream=None):
+    """Attention of every (token, head) query row of q bf16 [tokens, heads,
+    576] over every row of a gathered chunk; returns fp32 (o, lse)."""
+    return prepare_prefill_chunk_attention(q, chunk_kv, chunk_scale, softmax_scale, o, lse,
+                                           workspace, stream)()
+
+
+def prepare_prefill_chunk_attention(q, chunk_kv, chunk_scale, softmax_scale, o=None, lse=None,
+                                    workspace=None, stream=None):
+    """As prefill_chunk_attention, but returns a PreparedCall instead of calling."""
+    _need(q, torch.bfloat16, "q")
+    tokens, heads, _ = q.shape
+    kv_dtype = _kv_dtype(chunk_kv)
+    _need(chunk_kv, chunk_kv.dtype, "chunk_kv")
+    if chunk_kv.dim() != 2 or chunk_kv.shape[1] != HEAD_DIM:
+        raise ValueError(f"chunk_kv must be [chunk_len, {HEAD_DIM}]")
+    c = chunk_kv.shape[0]
+    if kv_dtype == KV_FP8_E4M3:
+        _need(chunk_scale, torch.float32, "chunk_scale", (c,))
+    if o is None:
+        o = torch.empty((tokens, heads, V_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((tokens, heads), dtype=torch.float32, device=q.device)
+    _need(o, torch.float32, "o", (tokens, heads, V_DIM))
+    _need(lse, torch.float32, "lse", (tokens, heads))
+    if workspace is None:
+        nb = prefill_workspace_size(tokens, heads, c)
+        workspace = alloc_workspace(nb, q.device) if nb else None
+    args = (_ptr(q), tokens, heads, _ptr(chunk_kv), _ptr(chunk_scale), c, kv_dtype,
+            float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace),
+            0 if workspace is None else workspace.numel(), _stream(q.device, stream))
+    return PreparedCall(lib().mla_prefill_chunk_lse, args, "mla_prefill_chunk_lse", (o, lse),
+                        q.device, (q, chunk_kv, chunk_scale, workspace))
+
+
+def merge_into(o_acc, lse_acc, o_new, lse_new, stream=None):
+    """Running merge in place: (o_acc, lse_acc) <- merge with (o_new, lse_new).
+    o_acc fp32 or bf16 [rows, heads, dv]; the others fp32."""
+    prepare_merge_into(o_acc, lse_acc, o_new, lse_new, stream)()
+
+
+def prepare_merge_into(o_acc, lse_acc, o_new, lse_new, stream=None):
+    """As merge_into, but returns a PreparedCall instead of calling."""
+    if o_acc.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("o_acc must be float32 or bfloat16")
+    _need(o_acc, o_acc.dtype, "o_acc")
+    rows, heads, dv = o_acc.shape
+    _need(lse_acc, torch.float32, "lse_acc", (rows, heads))
+    _need(o_new, torch.float32, "o_new", (rows, heads, dv))
+    _need(lse_new, torch.float32, "lse_new", (rows, heads))
+    acc_dtype = OUT_BF16 if o_acc.dtype == torch.bfloat16 else OUT_F32
+    args = (_ptr(o_acc), _ptr(lse_acc), _ptr(o_new), _ptr(lse_new), rows, heads, dv, acc_dtype,
+            _stream(o_acc.device, stream))
+    return PreparedCall(lib().lse_merge_into, args, "lse_merge_into", None, o_acc.device,
+                        (o_acc, lse_acc, o_new, lse_new))
+
+
+
+def prefix_attention(q, block_table_row, pools, scales, page_size, prefix_len, chunk, softmax_scale,
+                     acc_dtype=torch.float32, stream=None):
+    """The new tokens' attention to one sequence's cached prefix, the prefix
+    gathered from the shards in chunks of at most `chunk` tokens: for each
+    chunk, dcp_gather_prefix, mla_prefill_chunk_lse and lse_merge_into (the
+    running output kept in acc_dtype, float32 or bfloat16).  q bf16 [tokens,
+    heads, 576]; block_table_row int32 [max_pages] (device).  Only calls the
+    library; returns (o, lse)."""
+    tokens, heads, _ = q.shape
+    dev = q.device
+    o = torch.zeros((tokens, heads, V_DIM), dtype=acc_dtype, device=dev)
+    lse = torch.full((tokens, heads), float("-inf"), dtype=torch.float32, device=dev)
+    c_max = max(min(int(chunk), int(prefix_len)), 1)
+    kv = torch.empty((c_max, HEAD_DIM), dtype=pools[0].dtype, device=dev)
+    sc = torch.empty((c_max,), dtype=torch.float32, device=dev) \
+        if _kv_dtype(pools[0]) == KV_FP8_E4M3 else None
+    o_c = torch.empty((tokens, heads, V_DIM), dtype=torch.float32, device=dev)
+    lse_c = torch.empty((tokens, heads), dtype=torch.float32, device=dev)
+    ws_n = prefill_workspace_size(tokens, heads, c_max)
+    ws = alloc_workspace(ws_n, dev) if ws_n else None
+    bt = block_table_row.reshape(1, -1)
+    for b in range(0, int(prefix_len), int(chunk)):
+        n = min(int(chunk), int(prefix_len) - b)
+        gather_prefix(bt, pools, scales, page_size, [b], [n], out_kv=kv[:n],
+                      out_scale=None if sc is None else sc[:n], stream=stream)
+        prefill_chunk_attention(q, kv[:n], None if sc is None else sc[:n], softmax_scale, o_c, lse_c,
+                                workspace=ws, stream=stream)
+        merge_into(o, lse, o_c, lse_c, stream=stream)
+    return o, lse

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdcpmla.so")
 SOURCES = ["dcp_api.cpp", "dcp_remap.hip", "dcp_combine.hip", "dcp_decode.hip",
-           "dcp_decode_fp8.hip", "dcp_kv_write.hip", "dcp_noalloc.hip"]
+           "dcp_decode_fp8.hip", "dcp_kv_write.hip", "dcp_noalloc.hip",
+           "dcp_prefix.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

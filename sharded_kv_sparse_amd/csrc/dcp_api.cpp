@@ -248,6 +248,44 @@ dcp_status launch_checked(const DecodeParams& p, bool fp8, bool dense, hipStream
   return launch_decode(p, fp8, dense, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
 }
 
+// A prefill chunk's attention as dense decode launches: all query rows attend
+// the same chunk, so (token, head) rows are regrouped into rows of 64 heads
+// (tokens * heads / 64 of them; 64 heads per block read the chunk once), and
+// the tokens left over when 64 / heads does not divide the token count run as
+// a second launch with their own head count.
+struct PrefillLaunch {
+  long long rows;      // rows of this launch
+  int heads;           // heads per row
+  long long tok_off;   // first token of this launch
+};
+
+int prefill_launches(long long tokens, int heads, PrefillLaunch out[2]) {
+  int n = 0;
+  if (heads >= 64) {
+    out[n++] = PrefillLaunch{tokens * heads / 64, 64, 0};
+    return n;
+  }
+  const long long per = 64 / heads;               // tokens per 64-head row
+  const long long main_tok = tokens / per * per;
+  if (main_tok > 0) out[n++] = PrefillLaunch{main_tok / per, 64, 0};
+  if (tokens > main_tok) out[n++] = PrefillLaunch{tokens - main_tok, heads, main_tok};
+  return n;
+}
+
+size_t prefill_plan_bytes(long long tokens, int heads, long long chunk_len) {
+  PrefillLaunch l[2];
+  const int n = prefill_launches(tokens, heads, l);
+  size_t need = 0;
+  const int page = (int)std::max<long long>(chunk_len, 1);
+  for (int i = 0; i < n; ++i) {
+    int splits = 0;
+    if (plan_splits(true, l[i].rows, 1, l[i].heads, chunk_len, page, 0, &splits) != DCP_OK)
+      return std::numeric_limits<size_t>::max();
+    need = std::max(need, plan_workspace(l[i].rows, l[i].heads, 1, splits, true, false).total);
+  }
+  return need;
+}
+
 // The sparse decode call, with the caller's workspace or (noalloc) the
 // library's static scratch: counters at its start, partials after
 // kNoallocCounterBytes.
@@ -399,6 +437,108 @@ dcp_status mla_dense_decode_lse(const void* q, int64_t rows, int32_t heads,
   p.max_pages = max_pages;
   p.page_size = page_size;
   return launch_checked(p, kv_dtype == DCP_KV_FP8_E4M3, true, stream);
+}
+
+size_t dcp_prefill_workspace_size(int64_t tokens, int32_t heads, int64_t chunk_len) {
+  if (tokens < 0 || chunk_len < 0 || chunk_len > 0x7fffffffLL || !valid_heads(heads))
+    return std::numeric_limits<size_t>::max();
+  if (tokens == 0) return 0;
+  return prefill_plan_bytes(tokens, heads, chunk_len);
+}
+
+dcp_status mla_prefill_chunk_lse(const void* q, int64_t tokens, int32_t heads,
+                                 const void* chunk_kv, const float* chunk_scale,
+                                 int64_t chunk_len, dcp_kv_dtype kv_dtype, float softmax_scale,
+                                 float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (tokens < 0 || chunk_len < 0 || chunk_len > 0x7fffffffLL) return DCP_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != DCP_KV_BF16 && kv_dtype != DCP_KV_FP8_E4M3) return DCP_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DCP_ERR_INVALID_ARGUMENT;
+  if (tokens == 0) return DCP_OK;
+  if (!q || !o || !lse) return DCP_ERR_INVALID_ARGUMENT;
+  if (chunk_len == 0) {
+    // an empty chunk: the kernels read no KV row; the query stands in for the
+    // pool so that no address they form is null (one query row holds 1152 bytes)
+    if (!chunk_kv) chunk_kv = q;
+    if (!chunk_scale) chunk_scale = static_cast<const float*>(q);
+  }
+  if (!chunk_kv || (kv_dtype == DCP_KV_FP8_E4M3 && !chunk_scale)) return DCP_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(chunk_kv) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(chunk_scale) % 4 != 0)
+    return DCP_ERR_INVALID_ARGUMENT;
+  if (!valid_heads(heads)) return DCP_ERR_UNSUPPORTED;
+  const size_t need = prefill_plan_bytes(tokens, heads, chunk_len);
+  if (need == std::numeric_limits<size_t>::max()) return DCP_ERR_UNSUPPORTED;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DCP_ERR_WORKSPACE_TOO_SMALL;
+  dcp_kv_shard chunk{chunk_kv, chunk_scale, std::max<int64_t>(chunk_len, 1), nullptr, 0, 0};
+  PrefillLaunch l[2];
+  const int n = prefill_launches(tokens, heads, l);
+  for (int i = 0; i < n; ++i) {
+    const long long off = l[i].tok_off * heads;           // first (token, head) row
+    CommonArgs a{static_cast<const char*>(q) + off * kHeadDim * 2, l[i].rows, l[i].heads, &chunk, 1,
+                 kv_dtype, softmax_scale, o + off * kVDim, lse + off, nullptr, nullptr, DCP_OUT_F32, 0,
+                 workspace, workspace_bytes};
+    int splits = 0;
+    const int page = (int)std::max<int64_t>(chunk_len, 1);
+    dcp_status st = plan_splits(true, a.rows, 1, a.heads, chunk_len, page, 0, &splits);
+    if (st != DCP_OK) return st;
+    WorkspacePlan w = plan_workspace(a.rows, a.heads, 1, splits, true, false);
+    DecodeParams p = make_params(a, w);
+    p.block_table = nullptr;
+    p.max_pages = 1;
+    p.page_size = page;
+    p.chunk_mode = 1;
+    p.chunk_len = (int)chunk_len;
+    st = launch_checked(p, kv_dtype == DCP_KV_FP8_E4M3, true, stream);
+    if (st != DCP_OK) return st;
+  }
+  return DCP_OK;
+}
+
+dcp_status lse_merge_into(void* o_acc, float* lse_acc, const float* o_new, const float* lse_new,
+                          int64_t rows, int32_t heads, int32_t dv, dcp_out_dtype acc_dtype,
+                          hipStream_t stream) {
+  if (rows < 0 || heads < 1 || dv < 4 || dv % 4 != 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (acc_dtype != DCP_OUT_F32 && acc_dtype != DCP_OUT_BF16) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return DCP_OK;
+  if (!o_acc || !lse_acc || !o_new || !lse_new) return DCP_ERR_INVALID_ARGUMENT;
+  const size_t ea = acc_dtype == DCP_OUT_BF16 ? 8 : 16;
+  if (reinterpret_cast<uintptr_t>(o_acc) % ea != 0 || reinterpret_cast<uintptr_t>(o_new) % 16 != 0)
+    return DCP_ERR_INVALID_ARGUMENT;
+  if (rows * heads > 0x7fffffffLL * 4) return DCP_ERR_UNSUPPORTED;
+  return launch_merge_into(o_acc, lse_acc, o_new, lse_new, rows, heads, dv,
+                           acc_dtype == DCP_OUT_BF16, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
+dcp_status dcp_gather_prefix(const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                             const dcp_kv_shard* shards, int32_t num_shards, dcp_kv_dtype kv_dtype,
+                             const int32_t* pos_begin, const int32_t* out_offset, int32_t num_seqs,
+                             int32_t max_len, void* out_kv, float* out_scale, hipStream_t stream) {
+  if (num_seqs < 0 || max_len < 0 || num_shards < 1 || num_shards > kMaxShards)
+    return DCP_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != DCP_KV_BF16 && kv_dtype != DCP_KV_FP8_E4M3) return DCP_ERR_INVALID_ARGUMENT;
+  if (max_pages < 1 || page_size < 1) return DCP_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0 || max_len == 0) return DCP_OK;
+  if (!block_table || !pos_begin || !out_offset || !out_kv) return DCP_ERR_INVALID_ARGUMENT;
+  if (kv_dtype == DCP_KV_FP8_E4M3 && !out_scale) return DCP_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(out_kv) % 16 != 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (num_seqs > 65535) return DCP_ERR_UNSUPPORTED;
+  dcp_status st = check_shards(shards, num_shards, kv_dtype, false);
+  if (st != DCP_OK) return st;
+  GatherParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
+  p.num_shards = num_shards;
+  p.pos_begin = pos_begin;
+  p.out_offset = out_offset;
+  p.num_seqs = num_seqs;
+  p.out_kv = out_kv;
+  p.out_scale = out_scale;
+  for (int r = 0; r < num_shards; ++r) p.shard[r] = shard_arg(shards[r], kv_dtype);
+  return launch_gather_prefix(p, kv_dtype == DCP_KV_FP8_E4M3, max_len, stream) == hipSuccess
+             ? DCP_OK : DCP_ERR_LAUNCH;
 }
 
 dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_shards,

@@ -114,7 +114,8 @@ void decode_kernel(const DecodeParams p) {
   // ---- this block's token range [start, end) of the shard's local tokens
   int n_tok;
   if constexpr (DENSE) {
-    n_tok = (int)min((long long)sh.local_len[row], (long long)p.max_pages * p.page_size);
+    n_tok = p.chunk_mode ? p.chunk_len
+                         : (int)min((long long)sh.local_len[row], (long long)p.max_pages * p.page_size);
   } else {
     n_tok = min(p.counts[(long long)shard * p.rows + row], p.k);
   }
@@ -129,8 +130,9 @@ void decode_kernel(const DecodeParams p) {
   const int pg0 = DENSE ? start / page : 0;
   if constexpr (DENSE) {
     const int npg = end > start ? (end - 1) / page - pg0 + 1 : 0;
-    const int* bt = p.block_table + row * p.max_pages + pg0;
-    for (int i = tid; i < min(npg, kMaxList); i += NT) list[i] = bt[i];
+    // (a prefill chunk is one page, id 0, holding the whole chunk)
+    const int* bt = p.chunk_mode ? nullptr : p.block_table + row * p.max_pages + pg0;
+    for (int i = tid; i < min(npg, kMaxList); i += NT) list[i] = p.chunk_mode ? 0 : bt[i];
   } else {
     const int* src = p.topk_local + ((long long)shard * p.rows + row) * p.k + start;
     for (int i = tid; i < min(end - start, kMaxList); i += NT) list[i] = src[i];

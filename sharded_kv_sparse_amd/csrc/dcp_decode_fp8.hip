@@ -53,6 +53,9 @@ constexpr int kThreads = 256;
 
 template <bool B> struct BoolC { static constexpr bool value = B; };
 
+// The page table of a prefill chunk: one page, id 0, holding the whole chunk.
+__device__ int kChunkPage[1] = {0};
+
 // Chunk permutation of token t inside its 64-byte granule.
 __device__ __forceinline__ int chunk_sw(int t) { return ((t >> 1) ^ (t >> 3) ^ (t >> 4)) & 3; }
 
@@ -98,7 +101,8 @@ void decode_fp8_kernel(const DecodeParams p) {
   // ---- this block's token range [start, end) of the shard's local tokens
   int n_tok;
   if constexpr (DENSE) {
-    n_tok = (int)min((long long)sh.local_len[row], (long long)p.max_pages * p.page_size);
+    n_tok = p.chunk_mode ? p.chunk_len
+                         : (int)min((long long)sh.local_len[row], (long long)p.max_pages * p.page_size);
   } else {
     n_tok = min(p.counts[(long long)shard * p.rows + row], p.k);
   }
@@ -121,7 +125,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   // Where the id of local token j lives: the compacted slot id (sparse) or
   // the page id of its logical page (dense).
   const int page = DENSE ? p.page_size : 1;
-  const int* ids = DENSE ? p.block_table + row * p.max_pages
+  const int* ids = DENSE ? (p.chunk_mode ? kChunkPage : p.block_table + row * p.max_pages)
                          : p.topk_local + ((long long)shard * p.rows + row) * p.k;
   auto id_ptr = [&](int j) -> const int* { return DENSE ? ids + j / page : ids + j; };
   auto pool_row = [&](int j, int id) -> int {

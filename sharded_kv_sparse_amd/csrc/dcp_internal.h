@@ -62,6 +62,24 @@ struct DecodeParams {
   int* cnt_shard;                // [rows, N, head blocks]
   int xcd_swizzle;               // grid is a multiple of 8: keep a row's blocks on one XCD
   int merge_wait_ticks;          // >0: blocks wait up to this many 100 MHz ticks to share a merge
+  // dense, prefill chunk: every row attends tokens 0 .. chunk_len - 1 of one
+  // contiguous pool (no block table, no local_len; page_size >= chunk_len)
+  int chunk_mode;
+  int chunk_len;
+};
+
+// Arguments of the prefix gather kernel.
+struct GatherParams {
+  const int* block_table;        // [num_seqs, max_pages] DCP-wide logical pages
+  int max_pages;
+  int page_size;
+  int num_shards;
+  const int* pos_begin;          // [num_seqs] first position of each sequence's chunk
+  const int* out_offset;         // [num_seqs + 1] chunk rows of sequence b: out_offset[b] ..
+  int num_seqs;
+  void* out_kv;                  // [total, 576] codes or bf16
+  float* out_scale;              // [total] (FP8)
+  ShardArg shard[kMaxShards];
 };
 
 // Arguments of the KV-cache write kernel.
@@ -96,6 +114,10 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int num_sh
 hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeParams& p, bool dense, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, hipStream_t stream);
+
+hipError_t launch_gather_prefix(const GatherParams& p, bool fp8, int max_len, hipStream_t stream);
+hipError_t launch_merge_into(void* o_acc, float* lse_acc, const float* o_new, const float* lse_new,
+                             long long rows, int heads, int dv, int acc_bf16, hipStream_t stream);
 
 // Device address of this device's static scratch (looked up, and its counter
 // area cleared on `stream`, at the first call on each device).

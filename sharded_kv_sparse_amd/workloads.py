@@ -271,3 +271,70 @@ def make_workload(p, device="cpu", layers=1, seed=None):
         w.scales.append(scales)
         w.scales_host.append(scales_h)
     return w
+
+
+# ---------------------------------------------------------------------------
+# Prefill over a cached prefix (the new tokens of a sequence attend its cached
+# prefix, gathered from the shards in bounded chunks)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class PrefillPreset:
+    name: str
+    kv_dtype: str             # "bf16" | "fp8"
+    batch: int                # sequences
+    heads: int                # query heads of one rank
+    prefix: int               # cached tokens per sequence
+    new_tokens: int           # new (prefill) tokens per sequence
+    num_shards: int
+    chunk: int                # gathered chunk bound (tokens)
+    page_size: int = 64
+    sigma: float = 1.0 / math.sqrt(192.0)
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def lpages(self):
+        return -(-self.prefix // (self.page_size * self.num_shards))
+
+    @property
+    def pool_rows(self):
+        return self.batch * self.lpages * self.page_size
+
+    # the decode generator's view of the same cache (dense rows, one per sequence)
+    def as_dense(self):
+        return Preset(self.name, "dense", self.kv_dtype, batch=self.batch, q_per_seq=1,
+                      heads=self.heads, context=self.prefix, num_shards=self.num_shards,
+                      page_size=self.page_size, sigma=self.sigma, seed=self.seed)
+
+
+PREFILL_PRESETS = {
+    "prefill_fp8_prefix16k_new2k": PrefillPreset(
+        "prefill_fp8_prefix16k_new2k", "fp8", batch=1, heads=16, prefix=16384, new_tokens=2048,
+        num_shards=4, chunk=4096, seed=111,
+        note="prefill of 2,048 new tokens over a 16K cached prefix held by 4 shards, FP8 KV, "
+             "16 query heads, the prefix gathered in chunks of 4,096 tokens"),
+}
+
+
+@dataclass
+class PrefillWorkload:
+    p: PrefillPreset
+    cache: Workload           # block table, pools and scales of the cached prefix
+    q: torch.Tensor           # bf16 [batch, new_tokens, heads, 576]
+
+
+def make_prefill_workload(p, device="cpu"):
+    """The cached prefix (pools, scales, block table as for dense decode) and
+    the new tokens' queries, Q ~ N(0,1) rounded to bfloat16."""
+    if isinstance(p, str):
+        p = PREFILL_PRESETS[p]
+    cache = make_workload(p.as_dense(), device=device)
+    gen = _generator(device, p.seed + 7)
+    q = torch.randn((p.batch, p.new_tokens, p.heads, D_K), generator=gen, device=device).to(torch.bfloat16)
+    return PrefillWorkload(p=p, cache=cache, q=q)
+
+
+def prefix_chunks(p):
+    """[(begin, length)] of the bounded chunks covering a sequence's prefix."""
+    return [(b, min(p.chunk, p.prefix - b)) for b in range(0, p.prefix, p.chunk)]

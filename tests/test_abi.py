@@ -197,6 +197,60 @@ def test_merge_wait_setting_range(L):
     assert L.dcp_set_merge_wait_us(30) == OK
 
 
+def test_prefill_argument_checks(L):
+    def gather(bt=FAKE, max_pages=4, page=64, shards=None, n=2, kv=B.KV_FP8_E4M3, pb=FAKE, oo=FAKE,
+               seqs=2, max_len=100, out=FAKE, sc=FAKE):
+        return L.dcp_gather_prefix(bt, max_pages, page, _shards(2, fp8=True) if shards is None else shards,
+                                   n, kv, pb, oo, seqs, max_len, out, sc, None)
+    assert gather(seqs=0, bt=None) == OK                                 # nothing to gather
+    assert gather(max_len=0) == OK
+    assert gather(bt=None) == INVALID
+    assert gather(pb=None) == INVALID
+    assert gather(oo=None) == INVALID
+    assert gather(out=None) == INVALID
+    assert gather(sc=None) == INVALID                                    # FP8 needs the scales
+    assert gather(out=0x50008) == INVALID                                # not 16-byte aligned
+    assert gather(n=0) == INVALID
+    assert gather(page=0) == INVALID
+    assert gather(max_pages=0) == INVALID
+    assert gather(kv=9) == INVALID
+    assert gather(shards=_shards(2, fp8=False)) == INVALID
+    assert gather(seqs=70000) == UNSUPPORTED
+
+    def chunk(q=FAKE, tokens=37, heads=16, kv_ptr=FAKE, sc=FAKE, c=1000, kv=B.KV_FP8_E4M3, scale=0.07,
+              o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return L.mla_prefill_chunk_lse(q, tokens, heads, kv_ptr, sc, c, kv, scale, o, lse, ws, ws_bytes,
+                                       None)
+    assert chunk(tokens=0, q=None) == OK
+    assert chunk(q=None) == INVALID
+    assert chunk(kv_ptr=None) == INVALID
+    assert chunk(sc=None) == INVALID
+    assert chunk(o=None) == INVALID
+    assert chunk(lse=None) == INVALID
+    assert chunk(scale=0.0) == INVALID
+    assert chunk(c=-1) == INVALID
+    assert chunk(kv=4) == INVALID
+    assert chunk(heads=24) == UNSUPPORTED
+    assert chunk(kv_ptr=0x50008) == INVALID
+    bad = ctypes.c_size_t(-1).value
+    assert L.dcp_prefill_workspace_size(37, 24, 1000) == bad
+    assert L.dcp_prefill_workspace_size(-1, 16, 1000) == bad
+    assert L.dcp_prefill_workspace_size(0, 16, 1000) == 0
+    need = L.dcp_prefill_workspace_size(4, 16, 100000)                  # one row: split, workspace
+    assert need > 0 and chunk(tokens=4, c=100000, ws_bytes=need - 1) == WS_SMALL
+
+    def merge(o=FAKE, lse=FAKE, on=FAKE, ln=FAKE, rows=4, heads=16, dv=512, acc=B.OUT_F32):
+        return L.lse_merge_into(o, lse, on, ln, rows, heads, dv, acc, None)
+    assert merge(rows=0, o=None) == OK
+    assert merge(o=None) == INVALID
+    assert merge(ln=None) == INVALID
+    assert merge(dv=6) == INVALID
+    assert merge(acc=3) == INVALID
+    assert merge(heads=0) == INVALID
+    assert merge(o=0x50008) == INVALID                                   # fp32 accumulator: 16 bytes
+    assert merge(o=0x50004, acc=B.OUT_BF16) == INVALID                   # bf16 accumulator: 8 bytes
+
+
 def test_combine_argument_checks(L):
     f = L.lse_combine
     assert f(None, FAKE, 2, 4, 16, 512, FAKE, FAKE, 0, None) == INVALID

@@ -16,6 +16,7 @@ import oracle.dcp_oracle as real
 
 from . import test_oracle as pins
 from . import test_oracle_kvwrite as kv_pins
+from . import test_oracle_prefix as prefix_pins
 
 MUTATIONS = [
     ("value slice", "keys[:, :D_V]) / l", "keys[:, -D_V:]) / l"),
@@ -48,6 +49,13 @@ MUTATIONS = [
     ("quant divides by the scale", "q = (x * inv).astype(np.float32)", "q = (x / scale).astype(np.float32)"),
     ("kv write placement blocked", "r, row = int(g % num_shards), int(g // num_shards)",
      "r, row = int(g // pools[0].shape[0]), int(g % pools[0].shape[0])"),
+    ("prefix span without shards", "span = int(page_size) * int(num_shards)", "span = int(page_size)"),
+    ("prefix gather row by mod", "        r, row = g % n, g // n\n        rows[j]",
+     "        r, row = g // n % n, g % n\n        rows[j]"),
+    ("bf16 rounding truncates", "np.ldexp(np.rint(m * 256.0), e - 8)", "np.ldexp(np.trunc(m * 256.0), e - 8)"),
+    ("bf16 keeps 8 fraction bits", "np.ldexp(np.rint(m * 256.0), e - 8)", "np.ldexp(np.rint(m * 512.0), e - 9)"),
+    ("running merge drops the new chunk", "lse_merge(np.stack([o_acc, o_new]), np.stack([lse_acc, lse_new]))",
+     "lse_merge(np.stack([o_acc, o_acc]), np.stack([lse_acc, lse_new]))"),
     ("kv write keeps skipped", "        if g < 0:\n            continue\n        r, row",
      "        if g < -1:\n            continue\n        r, row"),
 ]
@@ -56,7 +64,8 @@ MUTATIONS = [
 def _pin_calls():
     calls = []
     for name, fn in inspect.getmembers(pins, inspect.isfunction) + \
-            inspect.getmembers(kv_pins, inspect.isfunction):
+            inspect.getmembers(kv_pins, inspect.isfunction) + \
+            inspect.getmembers(prefix_pins, inspect.isfunction):
         if not name.startswith("test_"):
             continue
         marks = getattr(fn, "pytestmark", [])
