@@ -28,4 +28,12 @@ from .dcp_oracle import (  # noqa: F401
     prefix_chunk_attention,
     round_bf16,
     merge_running,
+    D_INDEX,
+    index_scores,
+    topk_order,
+    index_local_topk,
+    merge_topk,
+    positions_to_slots,
+    sharded_topk,
+    unsharded_topk,
 )

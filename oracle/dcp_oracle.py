@@ -451,3 +451,112 @@ def merge_running(o_acc, lse_acc, o_new, lse_new, store_bf16=False):
     if store_bf16:
         o = round_bf16(o)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Sharded index cache and distributed top-k ([P3] "[DSA] Fix decode context
+# parallelism for RoPE sparse attention on Blackwell", Follow-ups, item 2:
+# the index keys -- 128 FP8 values and one fp32 scale per token, 132 bytes --
+# split across the ranks like the KV, each rank scoring its own tokens and
+# the local top-k candidates merged into the global top-k; [P1] "feat:
+# support decode context parallelism for PyTorch MLA", Summary, decode
+# bullet: local candidates merged into the global top-k, and File summaries:
+# distributed candidate packing and merging; review note: dcp * k a multiple
+# of 512 for the merge kernel.)
+#
+# The pages do not define the score.  Reading taken (the DSA indexer): for a
+# query row with index heads h (128-dim E4M3FN query codes q_h, fp32 weight
+# w_h) and a token with index key codes k_t and scale s_t > 0,
+#     score(t) = sum_h w_h * max(0, q_h . (s_t k_t)) = s_t * sum_h w_h * max(0, q_h . k_t).
+# Selection order: score descending, then position ascending (earlier
+# tokens first on equal scores); the global top-k is the first k positions
+# in that order, and its slots follow the cache's slot naming.
+# ---------------------------------------------------------------------------
+
+D_INDEX = 128
+
+
+def index_scores(q_codes, w, key_codes, key_scales):
+    """Scores of n tokens for one query row: q_codes uint8 [Hi, 128] (E4M3FN),
+    w [Hi], key_codes uint8 [n, 128], key_scales [n] (> 0).  Returns float64
+    [n]; the dot products of E4M3 values are exact in float64."""
+    q = _E4M3_TABLE[np.asarray(q_codes, dtype=np.uint8)]                   # [Hi, 128]
+    k = _E4M3_TABLE[np.asarray(key_codes, dtype=np.uint8)]                 # [n, 128]
+    # every product of two E4M3 values is a multiple of 2^-18 below 2^18, so
+    # the 128-term sums are exact in float64 whatever the summation order
+    dots = k @ q.T                                                          # [n, Hi]
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    s = np.asarray(key_scales, dtype=np.float32).astype(np.float64)
+    # the weighted sum over heads, per token in one fixed order (so a token's
+    # score does not depend on how many tokens are scored together)
+    return s * (np.maximum(dots, 0.0) * w[None, :]).sum(axis=1)
+
+
+def topk_order(scores, positions, k):
+    """Indices of the k best entries: score descending, then position
+    ascending; fewer when there are fewer entries."""
+    scores = np.asarray(scores, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    order = np.lexsort((positions, -scores))
+    return order[: int(k)]
+
+
+def index_local_topk(q_codes, w, index_pool, index_scale, block_table_row, n_local, page_size,
+                     num_shards, shard, k, score_fn=None):
+    """One shard's candidates for one query row: the scores of its local
+    tokens j < n_local (pool row BT[j div page] * page + j mod page, position
+    j * N + shard) and their top k.  score_fn(j_rows) may supply the scores
+    (e.g. float32 scores computed elsewhere).  Returns (scores [m], positions
+    [m]) in selection order, m = min(k, n_local)."""
+    rows = dense_local_rows(block_table_row, n_local, page_size)
+    if score_fn is None:
+        sc = index_scores(q_codes, w, np.asarray(index_pool)[rows], np.asarray(index_scale)[rows])
+    else:
+        sc = np.asarray(score_fn(rows), dtype=np.float64)
+    pos = np.arange(int(n_local), dtype=np.int64) * int(num_shards) + int(shard)
+    sel = topk_order(sc, pos, k)
+    return sc[sel], pos[sel]
+
+
+def merge_topk(cand_scores, cand_positions, k):
+    """The global top k of the shards' candidates (lists of (scores,
+    positions), one per shard), in selection order."""
+    sc = np.concatenate([np.asarray(c, dtype=np.float64) for c in cand_scores])
+    pos = np.concatenate([np.asarray(c, dtype=np.int64) for c in cand_positions])
+    sel = topk_order(sc, pos, k)
+    return sc[sel], pos[sel]
+
+
+def positions_to_slots(block_table_row, num_shards, page_size, positions):
+    """Slots of sequence positions (the slot naming of remap_topk)."""
+    return np.array([prefix_slot(block_table_row, num_shards, page_size, t) for t in positions],
+                    dtype=np.int64)
+
+
+def sharded_topk(q_codes, w, index_pools, index_scales, block_table_row, local_lens, page_size, k):
+    """Distributed top-k of one query row: every shard's local top-k, then
+    their merge.  local_lens[r]: tokens of the sequence held by shard r.
+    Returns (scores [m], positions [m], slots [m]) of the global top k."""
+    n = len(index_pools)
+    cs, cp = [], []
+    for r in range(n):
+        s, p = index_local_topk(q_codes, w, index_pools[r], index_scales[r], block_table_row,
+                                local_lens[r], page_size, n, r, k)
+        cs.append(s)
+        cp.append(p)
+    s, p = merge_topk(cs, cp, k)
+    return s, p, positions_to_slots(block_table_row, n, page_size, p)
+
+
+def unsharded_topk(q_codes, w, index_pools, index_scales, block_table_row, context, page_size, k):
+    """The same top k from one pass over every position of the sequence
+    (position t: shard t mod N, local token t div N)."""
+    n = len(index_pools)
+    sc = np.zeros(int(context))
+    for t in range(int(context)):
+        r, j = t % n, t // n
+        row = dense_local_rows(block_table_row, j + 1, page_size)[j]
+        sc[t] = index_scores(q_codes, w, np.asarray(index_pools[r])[row:row + 1],
+                             np.asarray(index_scales[r])[row:row + 1])[0]
+    sel = topk_order(sc, np.arange(int(context)), k)
+    return sc[sel], sel.astype(np.int64), positions_to_slots(block_table_row, n, page_size, sel)

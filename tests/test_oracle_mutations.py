@@ -17,6 +17,7 @@ import oracle.dcp_oracle as real
 from . import test_oracle as pins
 from . import test_oracle_kvwrite as kv_pins
 from . import test_oracle_prefix as prefix_pins
+from . import test_oracle_topk as topk_pins
 
 MUTATIONS = [
     ("value slice", "keys[:, :D_V]) / l", "keys[:, -D_V:]) / l"),
@@ -56,6 +57,14 @@ MUTATIONS = [
     ("bf16 keeps 8 fraction bits", "np.ldexp(np.rint(m * 256.0), e - 8)", "np.ldexp(np.rint(m * 512.0), e - 9)"),
     ("running merge drops the new chunk", "lse_merge(np.stack([o_acc, o_new]), np.stack([lse_acc, lse_new]))",
      "lse_merge(np.stack([o_acc, o_acc]), np.stack([lse_acc, lse_new]))"),
+    ("index ReLU dropped", "(np.maximum(dots, 0.0) * w[None, :])", "(dots * w[None, :])"),
+    ("index scale dropped", "return s * (np.maximum(dots, 0.0)", "return 1.0 * (np.maximum(dots, 0.0)"),
+    ("ties to the later position", "order = np.lexsort((positions, -scores))",
+     "order = np.lexsort((-positions, -scores))"),
+    ("local position by shard block", "pos = np.arange(int(n_local), dtype=np.int64) * int(num_shards) + int(shard)",
+     "pos = np.arange(int(n_local), dtype=np.int64) + int(shard) * int(n_local)"),
+    ("merge keeps the first shard only", "sc = np.concatenate([np.asarray(c, dtype=np.float64) for c in cand_scores])",
+     "sc = np.concatenate([np.asarray(c, dtype=np.float64) for c in cand_scores[:1]] + [np.full(len(c), -np.inf) for c in cand_scores[1:]])"),
     ("kv write keeps skipped", "        if g < 0:\n            continue\n        r, row",
      "        if g < -1:\n            continue\n        r, row"),
 ]
@@ -65,7 +74,8 @@ def _pin_calls():
     calls = []
     for name, fn in inspect.getmembers(pins, inspect.isfunction) + \
             inspect.getmembers(kv_pins, inspect.isfunction) + \
-            inspect.getmembers(prefix_pins, inspect.isfunction):
+            inspect.getmembers(prefix_pins, inspect.isfunction) + \
+            inspect.getmembers(topk_pins, inspect.isfunction):
         if not name.startswith("test_"):
             continue
         marks = getattr(fn, "pytestmark", [])
