@@ -95,7 +95,7 @@ def parse():
                     help="keep warming up (whole steps) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the prefill-over-a-cached-prefix timing")
+                    help="skip the timings of the prefill and of the distributed top-k")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the CPU-baseline sample (0 = all rows of one layer-step)")
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
@@ -257,6 +257,69 @@ def measure_prefill(stream, dev, reps=20, name="prefill_fp8_prefix16k_new2k"):
         "merge": {"kernel": "merge_into_kernel", "us_per_chunk": round(per[2], 2),
                   "gbps": round(m_bytes / (per[2] * 1e-6) / 1e9, 1),
                   "frac_hbm_peak": round(m_bytes / (per[2] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+
+
+def measure_topk(stream, dev, reps=20, name="index_topk_b64_ctx128k_k2048"):
+    """Time the sharded index cache and distributed top-k on its workload:
+    dcp_index_score (every local token of every (row, shard)), dcp_topk_local
+    and dcp_topk_merge, each over `reps` launches between events on the launch
+    stream, and the three back to back.  Algorithmic bytes of the scoring: 132
+    per token (128 codes + scale) + 4 (its score written) + the queries;
+    flops 2 x 128 x heads per token."""
+    p = wl.INDEX_PRESETS[name]
+    w = wl.make_index_workload(p, device=dev)
+    lens_dev = [w.dev(w.local_lens[r]) for r in range(p.num_shards)]
+    lens_all = w.dev(w.local_lens)
+    bt = w.dev(w.block_table)
+    scores = torch.empty((p.num_shards, p.rows, p.max_local), dtype=torch.float32, device=dev)
+    cs = torch.empty((p.num_shards, p.rows, p.topk), dtype=torch.float32, device=dev)
+    cp = torch.empty((p.num_shards, p.rows, p.topk), dtype=torch.int32, device=dev)
+    out = (torch.empty((p.rows, p.topk), dtype=torch.float32, device=dev),
+           torch.empty((p.rows, p.topk), dtype=torch.int32, device=dev),
+           torch.empty((p.rows, p.topk), dtype=torch.int32, device=dev))
+    calls = [B.prepare_index_score(w.q, w.w, w.keys, w.scales, lens_dev, bt, p.page_size, p.max_local,
+                                   out=scores, stream=stream),
+             B.prepare_topk_local(scores, lens_all, p.topk, cs, cp, stream=stream),
+             B.prepare_topk_merge(cs, cp, bt, p.page_size, out=out, stream=stream)]
+
+    def mk():
+        return torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    per = []
+    for f in calls:
+        t0, t1 = mk(), mk()
+        t0.record(stream)
+        for _ in range(reps):
+            f()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) * 1000.0 / reps)
+    t0, t1 = mk(), mk()
+    t0.record(stream)
+    for _ in range(reps):
+        for f in calls:
+            f()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    whole = t0.elapsed_time(t1) * 1000.0 / reps
+    tokens = int(w.local_lens.sum())
+    s_bytes = tokens * (132 + 4) + p.rows * p.index_heads * (128 + 4)
+    s_flops = 2.0 * 128 * p.index_heads * tokens
+    return {
+        "workload": p.name, "note": p.note, "us_per_layer": round(whole, 2),
+        "score": {"kernel": "index_score_kernel", "us": round(per[0], 2),
+                  "gbps": round(s_bytes / (per[0] * 1e-6) / 1e9, 1),
+                  "frac_hbm_peak": round(s_bytes / (per[0] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                  "tflops": round(s_flops / (per[0] * 1e-6) / 1e12, 1),
+                  "algorithmic_bytes": int(s_bytes)},
+        "local_topk": {"kernel": "topk_select_kernel (local)", "us": round(per[1], 2),
+                       "lists": p.rows * p.num_shards, "list_len": p.max_local},
+        "merge": {"kernel": "topk_select_kernel (merge)", "us": round(per[2], 2),
+                  "candidates_per_row": p.num_shards * p.topk},
     }
 
 
@@ -540,6 +603,8 @@ def main():
         del groups, prep
         torch.cuda.empty_cache()
         result["prefill_prefix"] = measure_prefill(stream, dev)
+        torch.cuda.empty_cache()
+        result["index_topk"] = measure_topk(stream, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: copying one layer to the host", file=sys.stderr, flush=True)
         w = groups[0]

@@ -50,6 +50,8 @@ extern "C" {
 #define DCP_HEAD_DIM 576
 #define DCP_V_DIM 512
 #define DCP_MAX_SHARDS 16
+#define DCP_INDEX_DIM 128
+#define DCP_MAX_TOPK 4096
 /* Static device scratch of mla_sparse_decode_lse_noalloc, per GPU: the
  * first DCP_NOALLOC_COUNTER_BYTES hold merge counters, the rest partials. */
 #define DCP_NOALLOC_SCRATCH_BYTES (64LL << 20)
@@ -268,6 +270,84 @@ dcp_status mla_dense_decode_lse(const void* q, int64_t rows, int32_t heads,
 dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_shards,
                        int64_t rows, int32_t heads, int32_t dv, void* o, float* lse,
                        dcp_out_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Sharded index cache and distributed top-k ([P3] "[DSA] Fix decode context
+ * parallelism for RoPE sparse attention on Blackwell", Follow-ups, item 2:
+ * the index keys -- 128 FP8 values and one fp32 scale per token -- split
+ * across the ranks like the KV, every rank scoring its own tokens, the local
+ * top-k candidates merged into the global top-k; [P1] "feat: support decode
+ * context parallelism for PyTorch MLA", Summary, decode bullet, and File
+ * summaries: distributed candidate packing and merging).
+ *
+ * One shard's index cache: token row r holds DCP_INDEX_DIM E4M3FN codes at
+ * (char*)keys + r * row_stride (0 = packed 128 bytes), its fp32 scale (> 0)
+ * at (char*)key_scale + r * scale_stride (0 = packed).  The rows follow the
+ * KV cache's paging: local token j of a sequence is row block_table[b][j /
+ * page_size] * page_size + j % page_size.  keys 16-byte aligned, row_stride
+ * a multiple of 16 >= 128, key_scale 4-byte aligned, scale_stride a multiple
+ * of 4.  local_len: device int32 [rows], the sequence's tokens on this shard.
+ */
+typedef struct dcp_index_shard {
+  const void* keys;
+  const float* key_scale;
+  int64_t pool_rows;
+  const int32_t* local_len;
+  int64_t row_stride;
+  int64_t scale_stride;
+} dcp_index_shard;
+
+/*
+ * Index scores of every local token of every (row, shard).  The pages give
+ * no score; the one computed (the DSA indexer form), for query row i with
+ * index heads h (E4M3FN codes q[i][h][0:128], fp32 weight w[i][h]):
+ *   score(j) = key_scale[j] * sum_h w[i][h] * max(0, q[i][h] . keys[j])
+ * in fp32 (the dot products on the fp8 MFMA: every product exact, the sums
+ * fp32; then the weighted sum over heads and the scale).
+ *   q        device uint8 [rows, index_heads, 128]; index_heads a multiple of
+ *            16, at most 128
+ *   w        device fp32 [rows, index_heads]
+ *   shards   host array of num_shards index caches (local_len required)
+ *   block_table  device int32 [rows, max_pages] (one query row per sequence)
+ *   scores   device fp32 [num_shards, rows, max_local]; entries j <
+ *            min(local_len, max_local) are written, the rest are left alone
+ */
+dcp_status dcp_index_score(const void* q, const float* w, int64_t rows, int32_t index_heads,
+                           const dcp_index_shard* shards, int32_t num_shards,
+                           const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                           int32_t max_local, float* scores, hipStream_t stream);
+
+/*
+ * Local top-k of every (row, shard): the first k of the shard's local tokens
+ * j < min(local_len[r][i], max_local) in the order score descending, then
+ * position ascending, where local token j of shard r is position j * N + r
+ * of its sequence (interleave 1).  Output in that order, padded with
+ * (-inf, -1) when a shard holds fewer than k tokens.
+ *   scores     device fp32 [num_shards, rows, max_local] (dcp_index_score)
+ *   local_len  device int32 [num_shards, rows]
+ *   cand_score, cand_pos  device fp32 / int32 [num_shards, rows, k]
+ *   1 <= k <= DCP_MAX_TOPK.
+ */
+dcp_status dcp_topk_local(const float* scores, int64_t rows, int32_t num_shards, int32_t max_local,
+                          const int32_t* local_len, int32_t k, float* cand_score, int32_t* cand_pos,
+                          hipStream_t stream);
+
+/*
+ * Merge of the shards' candidates into the global top-k of every row: the
+ * first k of the num_shards * k candidates (positions < 0 are padding) in the
+ * same order, with their slots (slot of position t: block_table[i][t div
+ * (page*N)] * page*N + t mod (page*N), the slot naming of dcp_remap_topk),
+ * padded with (-inf, -1, -1).  The pages' merge kernel needs num_shards * k
+ * to be a multiple of 512 ([P1] review note); the same is required here
+ * (else DCP_ERR_UNSUPPORTED).
+ *   cand_score, cand_pos  device [num_shards, rows, k] (dcp_topk_local)
+ *   top_score, top_pos  device fp32 / int32 [rows, k] (each may be NULL)
+ *   topk_global  device int32 [rows, k]: slots, the input of dcp_remap_topk
+ */
+dcp_status dcp_topk_merge(const float* cand_score, const int32_t* cand_pos, int64_t rows,
+                          int32_t num_shards, int32_t k, const int32_t* block_table,
+                          int32_t max_pages, int32_t page_size, float* top_score,
+                          int32_t* top_pos, int32_t* topk_global, hipStream_t stream);
 
 /*
  * Prefill over a cached prefix, step 1 -- gather ([P1] "feat: support decode

@@ -30,13 +30,20 @@ EXPORTS = ("dcp_status_string", "dcp_abi_version", "dcp_set_merge_wait_us", "dcp
            "dcp_decode_workspace_size", "mla_sparse_decode_lse", "mla_sparse_decode_lse_noalloc",
            "mla_dense_decode_lse",
            "lse_combine", "dcp_kv_write", "dcp_gather_prefix", "dcp_prefill_workspace_size",
-           "mla_prefill_chunk_lse", "lse_merge_into")
+           "mla_prefill_chunk_lse", "lse_merge_into", "dcp_index_score", "dcp_topk_local",
+           "dcp_topk_merge")
 
 
 class DcpError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
         super().__init__(f"{what}: {STATUS_NAMES.get(status, status)}")
+
+
+class IndexShard(ctypes.Structure):
+    _fields_ = [("keys", ctypes.c_void_p), ("key_scale", ctypes.c_void_p),
+                ("pool_rows", ctypes.c_int64), ("local_len", ctypes.c_void_p),
+                ("row_stride", ctypes.c_int64), ("scale_stride", ctypes.c_int64)]
 
 
 class KvShard(ctypes.Structure):
@@ -94,6 +101,13 @@ def lib():
     L.mla_prefill_chunk_lse.restype = ctypes.c_int
     L.lse_merge_into.argtypes = [vp, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
     L.lse_merge_into.restype = ctypes.c_int
+    L.dcp_index_score.argtypes = [vp, vp, i64, i32, ctypes.POINTER(IndexShard), i32, vp, i32, i32,
+                                  i32, vp, vp]
+    L.dcp_index_score.restype = ctypes.c_int
+    L.dcp_topk_local.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, vp]
+    L.dcp_topk_local.restype = ctypes.c_int
+    L.dcp_topk_merge.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, vp, vp, vp, vp]
+    L.dcp_topk_merge.restype = ctypes.c_int
     if L.dcp_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.dcp_abi_version()}, the binding "
                            f"expects {ABI_VERSION}: rebuild it")
@@ -534,3 +548,94 @@ def prefix_attention(q, block_table_row, pools, scales, page_size, prefix_len, c
                                 workspace=ws, stream=stream)
         merge_into(o, lse, o_c, lse_c, stream=stream)
     return o, lse
+
+
+# ---------------------------------------------------------------- sharded index cache + top-k
+
+def _index_shards(keys, scales, local_lens):
+    n = len(keys)
+    if not 1 <= n <= MAX_SHARDS:
+        raise ValueError("1..16 shards")
+    arr = (IndexShard * n)()
+    for r in range(n):
+        _need(keys[r], torch.uint8, f"keys[{r}]", contiguous=False)
+        if keys[r].dim() != 2 or keys[r].shape[1] != 128 or keys[r].stride(1) != 1:
+            raise ValueError(f"keys[{r}] must be [rows, 128] with unit inner stride")
+        _need(scales[r], torch.float32, f"key_scale[{r}]", (keys[r].shape[0],), contiguous=False)
+        _need(local_lens[r], torch.int32, f"local_len[{r}]")
+        arr[r] = IndexShard(keys[r].data_ptr(), scales[r].data_ptr(), keys[r].shape[0],
+                            local_lens[r].data_ptr(), keys[r].stride(0), scales[r].stride(0) * 4)
+    return arr
+
+
+def index_score(q, w, keys, scales, local_lens, block_table, page_size, max_local, out=None,
+                stream=None):
+    """Index scores [N, rows, max_local] fp32 of every local token: q uint8
+    [rows, hi, 128] E4M3FN codes, w fp32 [rows, hi], keys[r] uint8 [pool_rows,
+    128], scales[r] fp32 [pool_rows], local_lens[r] int32 [rows]."""
+    return prepare_index_score(q, w, keys, scales, local_lens, block_table, page_size, max_local,
+                               out, stream)()
+
+
+def prepare_index_score(q, w, keys, scales, local_lens, block_table, page_size, max_local, out=None,
+                        stream=None):
+    _need(q, torch.uint8, "q")
+    rows, hi, d = q.shape
+    if d != 128:
+        raise ValueError("index queries are [rows, heads, 128]")
+    _need(w, torch.float32, "w", (rows, hi))
+    _need(block_table, torch.int32, "block_table")
+    n = len(keys)
+    shards = _index_shards(keys, scales, local_lens)
+    if out is None:
+        out = torch.empty((n, rows, max_local), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "scores", (n, rows, max_local))
+    args = (_ptr(q), _ptr(w), rows, hi, shards, n, _ptr(block_table), block_table.shape[1],
+            int(page_size), int(max_local), _ptr(out), _stream(q.device, stream))
+    return PreparedCall(lib().dcp_index_score, args, "dcp_index_score", out, q.device,
+                        (q, w, keys, scales, local_lens, block_table))
+
+
+def topk_local(scores, local_len, k, cand_score=None, cand_pos=None, stream=None):
+    """Local top-k of every (shard, row): scores [N, rows, max_local],
+    local_len int32 [N, rows] -> (cand_score, cand_pos) [N, rows, k]."""
+    return prepare_topk_local(scores, local_len, k, cand_score, cand_pos, stream)()
+
+
+def prepare_topk_local(scores, local_len, k, cand_score=None, cand_pos=None, stream=None):
+    _need(scores, torch.float32, "scores")
+    n, rows, max_local = scores.shape
+    _need(local_len, torch.int32, "local_len", (n, rows))
+    if cand_score is None:
+        cand_score = torch.empty((n, rows, k), dtype=torch.float32, device=scores.device)
+    if cand_pos is None:
+        cand_pos = torch.empty((n, rows, k), dtype=torch.int32, device=scores.device)
+    _need(cand_score, torch.float32, "cand_score", (n, rows, k))
+    _need(cand_pos, torch.int32, "cand_pos", (n, rows, k))
+    args = (_ptr(scores), rows, n, max_local, _ptr(local_len), int(k), _ptr(cand_score), _ptr(cand_pos),
+            _stream(scores.device, stream))
+    return PreparedCall(lib().dcp_topk_local, args, "dcp_topk_local", (cand_score, cand_pos),
+                        scores.device, (scores, local_len))
+
+
+def topk_merge(cand_score, cand_pos, block_table, page_size, out=None, stream=None):
+    """Global top-k of every row from the shards' candidates [N, rows, k]:
+    returns (scores [rows, k], positions [rows, k], slots [rows, k])."""
+    return prepare_topk_merge(cand_score, cand_pos, block_table, page_size, out, stream)()
+
+
+def prepare_topk_merge(cand_score, cand_pos, block_table, page_size, out=None, stream=None):
+    _need(cand_score, torch.float32, "cand_score")
+    n, rows, k = cand_score.shape
+    _need(cand_pos, torch.int32, "cand_pos", (n, rows, k))
+    _need(block_table, torch.int32, "block_table")
+    dev = cand_score.device
+    if out is None:
+        out = (torch.empty((rows, k), dtype=torch.float32, device=dev),
+               torch.empty((rows, k), dtype=torch.int32, device=dev),
+               torch.empty((rows, k), dtype=torch.int32, device=dev))
+    ts, tp, tg = out
+    args = (_ptr(cand_score), _ptr(cand_pos), rows, n, k, _ptr(block_table), block_table.shape[1],
+            int(page_size), _ptr(ts), _ptr(tp), _ptr(tg), _stream(dev, stream))
+    return PreparedCall(lib().dcp_topk_merge, args, "dcp_topk_merge", out, dev,
+                        (cand_score, cand_pos, block_table))

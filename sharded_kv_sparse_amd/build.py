@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdcpmla.so")
 SOURCES = ["dcp_api.cpp", "dcp_remap.hip", "dcp_combine.hip", "dcp_decode.hip",
            "dcp_decode_fp8.hip", "dcp_kv_write.hip", "dcp_noalloc.hip",
-           "dcp_prefix.hip"]
+           "dcp_prefix.hip", "dcp_index_topk.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -541,6 +541,98 @@ dcp_status dcp_gather_prefix(const int32_t* block_table, int32_t max_pages, int3
              ? DCP_OK : DCP_ERR_LAUNCH;
 }
 
+dcp_status dcp_index_score(const void* q, const float* w, int64_t rows, int32_t index_heads,
+                           const dcp_index_shard* shards, int32_t num_shards,
+                           const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                           int32_t max_local, float* scores, hipStream_t stream) {
+  if (rows < 0 || num_shards < 1 || num_shards > kMaxShards || max_local < 0)
+    return DCP_ERR_INVALID_ARGUMENT;
+  if (index_heads < 16 || index_heads % 16 != 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (index_heads > kMaxIndexHeads) return DCP_ERR_UNSUPPORTED;
+  if (max_pages < 1 || page_size < 1) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows == 0 || max_local == 0) return DCP_OK;
+  if (!q || !w || !block_table || !scores || !shards) return DCP_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return DCP_ERR_INVALID_ARGUMENT;
+  IndexScoreParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int r = 0; r < num_shards; ++r) {
+    const dcp_index_shard& s = shards[r];
+    if (!s.keys || !s.key_scale || !s.local_len || s.pool_rows < 1) return DCP_ERR_INVALID_ARGUMENT;
+    if (reinterpret_cast<uintptr_t>(s.keys) % 16 != 0 || reinterpret_cast<uintptr_t>(s.key_scale) % 4 != 0)
+      return DCP_ERR_INVALID_ARGUMENT;
+    if (s.row_stride != 0 && (s.row_stride < kIndexDim || s.row_stride % 16 != 0))
+      return DCP_ERR_INVALID_ARGUMENT;
+    if (s.scale_stride < 0 || s.scale_stride % 4 != 0) return DCP_ERR_INVALID_ARGUMENT;
+    p.shard[r] = IndexShardArg{s.keys, s.key_scale, s.pool_rows, s.local_len,
+                               s.row_stride != 0 ? s.row_stride : kIndexDim,
+                               s.scale_stride != 0 ? s.scale_stride : 4};
+  }
+  p.q = static_cast<const unsigned char*>(q);
+  p.w = w;
+  p.rows = rows;
+  p.hi = index_heads;
+  p.num_shards = num_shards;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
+  p.max_local = max_local;
+  p.tiles_per_list = (max_local + index_score_tokens_per_block() - 1) / index_score_tokens_per_block();
+  p.scores = scores;
+  if (rows * num_shards * (long long)p.tiles_per_list > 0x7fffffffLL) return DCP_ERR_UNSUPPORTED;
+  return launch_index_score(p, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
+dcp_status dcp_topk_local(const float* scores, int64_t rows, int32_t num_shards, int32_t max_local,
+                          const int32_t* local_len, int32_t k, float* cand_score, int32_t* cand_pos,
+                          hipStream_t stream) {
+  if (rows < 0 || num_shards < 1 || num_shards > kMaxShards || max_local < 0)
+    return DCP_ERR_INVALID_ARGUMENT;
+  if (k < 1 || k > kMaxTopk) return DCP_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return DCP_OK;
+  if (!local_len || !cand_score || !cand_pos || (max_local > 0 && !scores))
+    return DCP_ERR_INVALID_ARGUMENT;
+  if ((long long)max_local * num_shards > 0x7fffffffLL) return DCP_ERR_UNSUPPORTED;
+  TopkParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.merge = 0;
+  p.rows = rows;
+  p.num_shards = num_shards;
+  p.k = k;
+  p.in_score = scores;
+  p.max_local = max_local;
+  p.local_len = local_len;
+  p.out_score = cand_score;
+  p.out_pos = cand_pos;
+  return launch_topk_select(p, rows * num_shards, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
+dcp_status dcp_topk_merge(const float* cand_score, const int32_t* cand_pos, int64_t rows,
+                          int32_t num_shards, int32_t k, const int32_t* block_table,
+                          int32_t max_pages, int32_t page_size, float* top_score,
+                          int32_t* top_pos, int32_t* topk_global, hipStream_t stream) {
+  if (rows < 0 || num_shards < 1 || num_shards > kMaxShards) return DCP_ERR_INVALID_ARGUMENT;
+  if (k < 1 || k > kMaxTopk || max_pages < 1 || page_size < 1) return DCP_ERR_INVALID_ARGUMENT;
+  if (((long long)num_shards * k) % 512 != 0) return DCP_ERR_UNSUPPORTED;
+  if (rows == 0) return DCP_OK;
+  if (!cand_score || !cand_pos || !block_table || !topk_global) return DCP_ERR_INVALID_ARGUMENT;
+  TopkParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.merge = 1;
+  p.rows = rows;
+  p.num_shards = num_shards;
+  p.k = k;
+  p.in_score = cand_score;
+  p.in_pos = cand_pos;
+  p.k_in = k;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page_size = page_size;
+  p.out_score = top_score;
+  p.out_pos = top_pos;
+  p.out_slot = topk_global;
+  return launch_topk_select(p, rows, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+}
+
 dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_shards,
                        int64_t rows, int32_t heads, int32_t dv, void* o, float* lse,
                        dcp_out_dtype out_dtype, hipStream_t stream) {

@@ -1,0 +1,297 @@
+// Sharded index cache and distributed top-k: every shard scores its own
+// tokens' index keys and keeps its local top-k; the shards' candidates are
+// merged into the global top-k, whose slots feed the index remap.
+//
+// Pages: [P3] "[DSA] Fix decode context parallelism for RoPE sparse attention
+// on Blackwell", Follow-ups item 2 (index keys of 128 FP8 values + one fp32
+// scale per token, 132 bytes, split across the ranks like the KV; the local
+// top-k candidates merged by one more collective per indexer layer); [P1]
+// "feat: support decode context parallelism for PyTorch MLA", Summary (DSA
+// merges local candidates into the global top-k), File summaries
+// (distributed candidate packing and merging) and the review note that the
+// merge needs dcp * k to be a multiple of 512.
+//
+// Score (the DSA indexer form; the pages give none): for a query row with
+// index heads h (E4M3FN codes q_h, fp32 weight w_h) and a token with index
+// key codes k_t and scale s_t > 0,
+//     score(t) = s_t * sum_h w_h * max(0, q_h . k_t),
+// with q_h . k_t on the fp8 MFMA (16 tokens x 16 heads x 128 dims per
+// instruction; every product of two E4M3 values is exact, the sums fp32).
+// One wave scores 64 tokens (four 16-token groups); its A operands come
+// straight from global memory (a token's 128-byte key row is one line, and
+// the 16 tokens of a group are contiguous rows of a page).
+//
+// Selection: score descending, then position ascending, as one 64-bit key
+// (the order-preserving image of the fp32 score above the complement of the
+// position), so every key is distinct and the top k is unique.  One block
+// per list finds the k-th largest key by radix select (eight 8-bit digits,
+// histograms in LDS, the list re-read from L2 per pass), gathers the keys
+// above it and sorts them (bitonic, in LDS).
+#include "dcp_device.h"
+#include "dcp_internal.h"
+
+namespace dcp {
+namespace {
+
+constexpr int kScoreThreads = 256;                 // 4 waves x 64 tokens
+constexpr int kScoreTokens = 256;
+constexpr int kSelectThreads = 1024;
+
+// ---------------------------------------------------------------- scores
+
+__global__ __launch_bounds__(kScoreThreads) void index_score_kernel(IndexScoreParams p) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  long long b = blockIdx.x;
+  const int tiles = p.tiles_per_list;
+  const int tile = (int)(b % tiles);
+  b /= tiles;
+  const int shard = (int)(b % p.num_shards);
+  const long long row = b / p.num_shards;
+  const IndexShardArg sh = p.shard[shard];
+  const int n_local = min(max(sh.local_len[row], 0), p.max_local);
+  const int t0 = tile * kScoreTokens + wave * 64;
+  if (t0 >= n_local) return;
+
+  // query operands (B of S^T = K Q^T): head group hg, lane (head i16, g) holds
+  // dims 16g .. +16 (bytes 0..15) and 64 + 16g .. +16 (bytes 16..31)
+  typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+  const unsigned char* qrow = p.q + (size_t)row * p.hi * kIndexDim;
+  const float* wrow = p.w + (size_t)row * p.hi;
+  const int HG = p.hi / 16;
+  i32x8 qb[kMaxIndexHeads / 16];
+  float wv[kMaxIndexHeads / 16];
+#pragma unroll
+  for (int hg = 0; hg < kMaxIndexHeads / 16; ++hg) {
+    if (hg < HG) {
+      const unsigned char* qh = qrow + (size_t)(16 * hg + i16) * kIndexDim;
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(qh + 16 * g);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(qh + 64 + 16 * g);
+      qb[hg] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      wv[hg] = wrow[16 * hg + i16];
+    } else {
+      qb[hg] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      wv[hg] = 0.f;
+    }
+  }
+  const int* bt = p.block_table + row * p.max_pages;
+  const long long max_prow = sh.pool_rows - 1;
+  auto pool_row = [&](int j) -> long long {
+    const int pg = min(j / p.page_size, p.max_pages - 1);
+    const long long r = (long long)bt[pg] * p.page_size + (j - (j / p.page_size) * p.page_size);
+    return min(max(r, 0LL), max_prow);
+  };
+  const char* keys = static_cast<const char*>(sh.keys);
+  const char* scl = reinterpret_cast<const char*>(sh.scale);
+
+  // all four groups' key loads first, then the MFMAs
+  i32x8 ka[4];
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    const int j = t0 + 16 * grp + i16;
+    const char* kr = keys + pool_row(min(j, n_local - 1)) * sh.row_stride;
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kr + 16 * g);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kr + 64 + 16 * g);
+    ka[grp] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  // scales of the four tokens 16 grp + 4g + i this lane sums for (lanes with i16 = 0)
+  float sc[4][4];
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = min(t0 + 16 * grp + 4 * g + i, n_local - 1);
+      sc[grp][i] = i16 == 0 ? *reinterpret_cast<const float*>(scl + pool_row(j) * sh.scale_stride) : 0.f;
+    }
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    // lane (head i16, g): tokens 4g .. 4g + 3 of the group, summed over head groups
+    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hg = 0; hg < kMaxIndexHeads / 16; ++hg) {
+      if (hg < HG) {
+        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            ka[grp], qb[hg], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[i] += wv[hg] * fmaxf(d[i], 0.f);
+      }
+    }
+    // sum over the 16 heads of the group's lanes (xor over lane bits 0..3)
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], m, 64);
+    if (i16 == 0) {
+      const int j0 = t0 + 16 * grp + 4 * g;
+      float* out = p.scores + ((long long)shard * p.rows + row) * p.max_local + j0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j0 + i < n_local) out[i] = sc[grp][i] * part[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- selection
+
+// Order-preserving image of an fp32 score (larger score, larger key).
+__device__ __forceinline__ unsigned score_bits(float s) {
+  const unsigned u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float bits_score(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ unsigned long long make_key(float s, int pos) {
+  const float v = s == 0.f ? 0.f : s;               // -0 ranks as +0 (they are equal scores)
+  return ((unsigned long long)score_bits(v) << 32) | (unsigned)(0xffffffffu - (unsigned)pos);
+}
+
+// Element e of list `list`: its key, or 0 (below every real key: position
+// 0xffffffff never occurs) when it is not a candidate.
+struct ListSource {
+  const TopkParams& p;
+  long long list;
+  int n;
+  __device__ unsigned long long key(int e) const {
+    if (p.merge) {
+      const long long row = list;
+      const int r = e / p.k_in, idx = e - r * p.k_in;
+      const long long at = ((long long)r * p.rows + row) * p.k_in + idx;
+      const int pos = p.in_pos[at];
+      return pos >= 0 ? make_key(p.in_score[at], pos) : 0ull;
+    }
+    const int shard = (int)(list / p.rows);
+    return make_key(p.in_score[list * p.max_local + e], e * p.num_shards + shard);
+  }
+};
+
+__global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(TopkParams p) {
+  __shared__ unsigned hist[256];
+  __shared__ unsigned long long s_prefix;
+  __shared__ unsigned s_need, s_count;
+  __shared__ unsigned long long sel[kMaxTopk];
+  const int tid = threadIdx.x;
+  const long long list = blockIdx.x;
+  int n;
+  if (p.merge) {
+    n = p.num_shards * p.k_in;
+  } else {
+    const int shard = (int)(list / p.rows);
+    const long long row = list - (long long)shard * p.rows;
+    n = min(max(p.local_len[(long long)shard * p.rows + row], 0), p.max_local);
+  }
+  const ListSource src{p, list, n};
+  const int k = p.k;
+
+  // ---- count the candidates (merge lists may hold padding)
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+  unsigned mine = 0;
+  for (int e = tid; e < n; e += kSelectThreads) mine += src.key(e) != 0ull;
+  atomicAdd(&s_count, mine);
+  __syncthreads();
+  const unsigned valid = s_count;
+
+  // ---- the k-th largest key (all keys are distinct), digit by digit
+  unsigned long long thresh = 1ull;                 // every candidate when valid <= k
+  if (valid > (unsigned)k) {
+    if (tid == 0) { s_prefix = 0ull; s_need = (unsigned)k; }
+    unsigned long long mask = 0ull;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0;
+      __syncthreads();
+      const unsigned long long prefix = s_prefix;
+      for (int e = tid; e < n; e += kSelectThreads) {
+        const unsigned long long kv = src.key(e);
+        if (kv != 0ull && (kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned need = s_need, above = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (above + hist[d] >= need) break;
+          above += hist[d];
+        }
+        s_need = need - above;
+        s_prefix = prefix | ((unsigned long long)d << shift);
+      }
+      mask |= 255ull << shift;
+      __syncthreads();
+    }
+    thresh = s_prefix;
+  }
+
+  // ---- gather the selected keys, then sort them (descending)
+  const unsigned m = valid < (unsigned)k ? valid : (unsigned)k;
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+  for (int e = tid; e < n; e += kSelectThreads) {
+    const unsigned long long kv = src.key(e);
+    if (kv != 0ull && kv >= thresh) {
+      const unsigned at = atomicAdd(&s_count, 1u);
+      if (at < m) sel[at] = kv;                     // exactly m pass (keys are distinct)
+    }
+  }
+  __syncthreads();
+  int np2 = 1;
+  while (np2 < (int)m) np2 <<= 1;
+  for (int i = (int)m + tid; i < np2; i += kSelectThreads) sel[i] = 0ull;
+  __syncthreads();
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < np2 / 2; i += kSelectThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const unsigned long long a = sel[lo], c = sel[hi];
+        if ((a < c) == desc) {
+          sel[lo] = c;
+          sel[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- write the list's top k in order, padded with (-inf, -1)
+  for (int i = tid; i < k; i += kSelectThreads) {
+    float s = kNegInf;
+    int pos = -1;
+    if (i < (int)m) {
+      const unsigned long long kv = sel[i];
+      s = bits_score((unsigned)(kv >> 32));
+      pos = (int)(0xffffffffu - (unsigned)(kv & 0xffffffffull));
+    }
+    if (p.out_score) p.out_score[list * k + i] = s;
+    if (p.out_pos) p.out_pos[list * k + i] = pos;
+    if (p.out_slot) {
+      int slot = -1;
+      if (pos >= 0) {
+        const long long span = (long long)p.page_size * p.num_shards;
+        const long long lp = min((long long)pos / span, (long long)p.max_pages - 1);
+        slot = (int)((long long)p.block_table[list * p.max_pages + lp] * span + pos % span);
+      }
+      p.out_slot[list * k + i] = slot;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_score(const IndexScoreParams& p, hipStream_t stream) {
+  const long long blocks = p.rows * p.num_shards * (long long)p.tiles_per_list;
+  void* args[] = {(void*)&p};
+  return hipLaunchKernel((const void*)index_score_kernel, dim3((unsigned)blocks), dim3(kScoreThreads),
+                         args, 0, stream);
+}
+
+hipError_t launch_topk_select(const TopkParams& p, long long lists, hipStream_t stream) {
+  void* args[] = {(void*)&p};
+  return hipLaunchKernel((const void*)topk_select_kernel, dim3((unsigned)lists), dim3(kSelectThreads),
+                         args, 0, stream);
+}
+
+int index_score_tokens_per_block() { return kScoreTokens; }
+
+}  // namespace dcp

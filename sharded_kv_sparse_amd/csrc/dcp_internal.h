@@ -68,6 +68,58 @@ struct DecodeParams {
   int chunk_len;
 };
 
+// Index cache of one shard (the DSA indexer's keys): 128 E4M3FN codes per
+// token at a row stride, one fp32 scale per token at a scale stride.
+constexpr int kIndexDim = DCP_INDEX_DIM;
+constexpr int kMaxIndexHeads = 128;
+constexpr int kMaxTopk = 4096;
+struct IndexShardArg {
+  const void* keys;
+  const float* scale;
+  long long pool_rows;
+  const int* local_len;          // [rows]
+  long long row_stride;          // bytes (resolved, never 0)
+  long long scale_stride;        // bytes (resolved, never 0)
+};
+
+struct IndexScoreParams {
+  const unsigned char* q;        // [rows, hi, 128] E4M3FN
+  const float* w;                // [rows, hi]
+  long long rows;
+  int hi;                        // index heads, a multiple of 16
+  int num_shards;
+  const int* block_table;        // [rows, max_pages]
+  int max_pages;
+  int page_size;
+  int max_local;                 // row length of scores
+  int tiles_per_list;
+  float* scores;                 // [N, rows, max_local]
+  IndexShardArg shard[kMaxShards];
+};
+
+// Top-k selection over lists of (score, position): local (a shard's scores,
+// position = j * N + shard) or merge (the shards' candidates of a row).
+struct TopkParams {
+  int merge;
+  long long rows;
+  int num_shards;
+  int k;                         // output width
+  // local
+  const float* in_score;         // local: [N, rows, max_local]; merge: [N, rows, k_in]
+  int max_local;
+  const int* local_len;          // [N, rows]
+  // merge
+  const int* in_pos;             // [N, rows, k_in]
+  int k_in;
+  const int* block_table;        // [rows, max_pages] (merge: positions -> slots)
+  int max_pages;
+  int page_size;
+  // outputs [lists, k]
+  float* out_score;
+  int* out_pos;
+  int* out_slot;                 // merge only, may be null
+};
+
 // Arguments of the prefix gather kernel.
 struct GatherParams {
   const int* block_table;        // [num_seqs, max_pages] DCP-wide logical pages
@@ -115,6 +167,9 @@ hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_
 hipError_t launch_decode_fp8(const DecodeParams& p, bool dense, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, hipStream_t stream);
 
+hipError_t launch_index_score(const IndexScoreParams& p, hipStream_t stream);
+hipError_t launch_topk_select(const TopkParams& p, long long lists, hipStream_t stream);
+int index_score_tokens_per_block();
 hipError_t launch_gather_prefix(const GatherParams& p, bool fp8, int max_len, hipStream_t stream);
 hipError_t launch_merge_into(void* o_acc, float* lse_acc, const float* o_new, const float* lse_new,
                              long long rows, int heads, int dv, int acc_bf16, hipStream_t stream);

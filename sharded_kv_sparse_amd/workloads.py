@@ -338,3 +338,94 @@ def make_prefill_workload(p, device="cpu"):
 def prefix_chunks(p):
     """[(begin, length)] of the bounded chunks covering a sequence's prefix."""
     return [(b, min(p.chunk, p.prefix - b)) for b in range(0, p.prefix, p.chunk)]
+
+
+# ---------------------------------------------------------------------------
+# Sharded index cache (the DSA indexer's keys, split over the shards like the
+# KV) and its query rows
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class IndexPreset:
+    name: str
+    batch: int                # sequences, one query row each
+    context: int              # tokens per sequence
+    num_shards: int
+    index_heads: int = 64
+    topk: int = 2048
+    page_size: int = 64
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def rows(self):
+        return self.batch
+
+    def as_dense(self):
+        return Preset(self.name, "dense", "fp8", batch=self.batch, q_per_seq=1, heads=16,
+                      context=self.context, num_shards=self.num_shards, page_size=self.page_size,
+                      seed=self.seed)
+
+    @property
+    def pool_rows(self):
+        return self.as_dense().pool_rows
+
+    @property
+    def max_local(self):
+        return -(-self.context // self.num_shards)
+
+
+INDEX_PRESETS = {
+    "index_topk_b64_ctx128k_k2048": IndexPreset(
+        "index_topk_b64_ctx128k_k2048", batch=64, context=131072, num_shards=4, index_heads=64,
+        topk=2048, seed=106,
+        note="sharded index cache + distributed top-k: 64 rows, 128K context over 4 shards, "
+             "64 index heads x 128 FP8 dims + fp32 scale per token (132 bytes), top-k 2048"),
+}
+
+
+@dataclass
+class IndexWorkload:
+    p: IndexPreset
+    block_table: np.ndarray   # [batch, lpages]
+    local_lens: np.ndarray    # [N, batch]
+    q: torch.Tensor           # uint8 [rows, hi, 128] E4M3FN codes
+    w: torch.Tensor           # fp32 [rows, hi]
+    keys: list                # [N] uint8 [pool_rows, 128]
+    scales: list              # [N] fp32 [pool_rows]
+    scales_host: list
+    device: str = "cpu"
+
+    def dev(self, arr, dtype=torch.int32):
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(self.device, dtype)
+
+
+def make_index_workload(p, device="cpu", empty_shard_rows=False):
+    """Index keys: E4M3FN codes of N(0,1) draws (torch's conversion), one fp32
+    scale 2^U(-6, 2) per token; queries: E4M3FN codes of N(0,1); weights
+    N(0,1) / sqrt(heads).  Paging and local lengths as for dense decode.
+    empty_shard_rows: rows with b mod 4 == 0 give shard (b / 4) mod N no tokens."""
+    if isinstance(p, str):
+        p = INDEX_PRESETS[p]
+    d = p.as_dense()
+    rng = np.random.default_rng(p.seed)
+    bt = make_block_table(d, rng)
+    lens = make_local_lens(replace(d, forced_empty=empty_shard_rows))
+    gen = _generator(device, p.seed)
+    q = torch.randn((p.rows, p.index_heads, 128), generator=gen, device=device) \
+        .to(torch.float8_e4m3fn).view(torch.uint8)
+    w = (torch.randn((p.rows, p.index_heads), generator=gen, device=device)
+         / math.sqrt(p.index_heads)).float()
+    keys, scales, scales_h = [], [], []
+    for _ in range(p.num_shards):
+        k = torch.empty((d.pool_rows, 128), dtype=torch.uint8, device=device)
+        for s in range(0, d.pool_rows, 1 << 18):
+            e = min(d.pool_rows, s + (1 << 18))
+            k[s:e] = torch.randn((e - s, 128), generator=gen, device=device) \
+                .to(torch.float8_e4m3fn).view(torch.uint8)
+        keys.append(k)
+        sh = make_scales(d, rng)
+        scales_h.append(sh)
+        scales.append(torch.from_numpy(sh).to(device))
+    return IndexWorkload(p=p, block_table=bt, local_lens=lens, q=q, w=w, keys=keys, scales=scales,
+                         scales_host=scales_h, device=device)
