@@ -340,7 +340,9 @@ dcp_status dcp_topk_local(const float* scores, int64_t rows, int32_t num_shards,
  * padded with (-inf, -1, -1).  The pages' merge kernel needs num_shards * k
  * to be a multiple of 512 ([P1] review note); the same is required here
  * (else DCP_ERR_UNSUPPORTED).
- *   cand_score, cand_pos  device [num_shards, rows, k] (dcp_topk_local)
+ *   cand_score, cand_pos  device [num_shards, rows, k], each shard's list in
+ *                selection order with its padding last (as dcp_topk_local
+ *                writes them; the merge relies on that order)
  *   top_score, top_pos  device fp32 / int32 [rows, k] (each may be NULL)
  *   topk_global  device int32 [rows, k]: slots, the input of dcp_remap_topk
  */

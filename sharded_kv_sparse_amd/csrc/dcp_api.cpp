@@ -630,7 +630,7 @@ dcp_status dcp_topk_merge(const float* cand_score, const int32_t* cand_pos, int6
   p.out_score = top_score;
   p.out_pos = top_pos;
   p.out_slot = topk_global;
-  return launch_topk_select(p, rows, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
+  return launch_topk_merge(p, rows, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
 }
 
 dcp_status lse_combine(const float* o_part, const float* lse_part, int32_t num_shards,

@@ -33,8 +33,10 @@
 namespace dcp {
 namespace {
 
-constexpr int kScoreThreads = 256;                 // 4 waves x 64 tokens
-constexpr int kScoreTokens = 256;
+constexpr int kScoreThreads = 256;                 // 4 waves
+constexpr int kScoreWaveGroups = 16;               // 16-token groups per wave
+constexpr int kScoreBatch = 8;                     // groups loaded together
+constexpr int kScoreTokens = 4 * 16 * kScoreWaveGroups;   // 1024 tokens per block
 constexpr int kSelectThreads = 1024;
 
 // ---------------------------------------------------------------- scores
@@ -50,11 +52,12 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(IndexScorePa
   const long long row = b / p.num_shards;
   const IndexShardArg sh = p.shard[shard];
   const int n_local = min(max(sh.local_len[row], 0), p.max_local);
-  const int t0 = tile * kScoreTokens + wave * 64;
+  const int t0 = tile * kScoreTokens + wave * (16 * kScoreWaveGroups);
   if (t0 >= n_local) return;
 
   // query operands (B of S^T = K Q^T): head group hg, lane (head i16, g) holds
-  // dims 16g .. +16 (bytes 0..15) and 64 + 16g .. +16 (bytes 16..31)
+  // bytes 16g .. +16 and 64 + 16g .. +16 of its head's 128 codes (the keys'
+  // A operands take the same bytes, so the products pair up)
   typedef __attribute__((ext_vector_type(4))) int i32x4_t;
   const unsigned char* qrow = p.q + (size_t)row * p.hi * kIndexDim;
   const float* wrow = p.w + (size_t)row * p.hi;
@@ -83,50 +86,55 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(IndexScorePa
   };
   const char* keys = static_cast<const char*>(sh.keys);
   const char* scl = reinterpret_cast<const char*>(sh.scale);
+  float* out_row = p.scores + ((long long)shard * p.rows + row) * p.max_local;
 
-  // all four groups' key loads first, then the MFMAs
-  i32x8 ka[4];
+  for (int gb = 0; gb < kScoreWaveGroups; gb += kScoreBatch) {
+    if (t0 + 16 * gb >= n_local) break;
+    // the batch's key rows and scales first (lane: token 16 grp + i16)
+    i32x8 ka[kScoreBatch];
+    float scv[kScoreBatch];
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) {
-    const int j = t0 + 16 * grp + i16;
-    const char* kr = keys + pool_row(min(j, n_local - 1)) * sh.row_stride;
-    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kr + 16 * g);
-    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kr + 64 + 16 * g);
-    ka[grp] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  }
-  // scales of the four tokens 16 grp + 4g + i this lane sums for (lanes with i16 = 0)
-  float sc[4][4];
-#pragma unroll
-  for (int grp = 0; grp < 4; ++grp)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = min(t0 + 16 * grp + 4 * g + i, n_local - 1);
-      sc[grp][i] = i16 == 0 ? *reinterpret_cast<const float*>(scl + pool_row(j) * sh.scale_stride) : 0.f;
+    for (int u = 0; u < kScoreBatch; ++u) {
+      const int j = min(t0 + 16 * (gb + u) + i16, n_local - 1);
+      const long long pr = pool_row(j);
+      const char* kr = keys + pr * sh.row_stride;
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kr + 16 * g);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kr + 64 + 16 * g);
+      ka[u] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      scv[u] = *reinterpret_cast<const float*>(scl + pr * sh.scale_stride);
     }
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) {
-    // lane (head i16, g): tokens 4g .. 4g + 3 of the group, summed over head groups
-    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kScoreBatch; ++u) {
+      // lane (head i16, g): tokens 4g .. 4g + 3 of the group, summed over head groups
+      f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int hg = 0; hg < kMaxIndexHeads / 16; ++hg) {
-      if (hg < HG) {
-        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            ka[grp], qb[hg], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+      for (int hg = 0; hg < kMaxIndexHeads / 16; ++hg) {
+        if (hg < HG) {
+          const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              ka[u], qb[hg], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[i] += wv[hg] * fmaxf(d[i], 0.f);
+          for (int i = 0; i < 4; ++i) part[i] += wv[hg] * fmaxf(d[i], 0.f);
+        }
       }
-    }
-    // sum over the 16 heads of the group's lanes (xor over lane bits 0..3)
+      // sum over the 16 heads of the group's lanes (xor over lane bits 0..3)
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
+      for (int m = 1; m < 16; m <<= 1)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], m, 64);
-    if (i16 == 0) {
-      const int j0 = t0 + 16 * grp + 4 * g;
-      float* out = p.scores + ((long long)shard * p.rows + row) * p.max_local + j0;
+        for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], m, 64);
+      // token 4g + i's scale sits in lane 4g + i (its A row)
+      f32x4 res;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (j0 + i < n_local) out[i] = sc[grp][i] * part[i];
+      for (int i = 0; i < 4; ++i) res[i] = __shfl(scv[u], 4 * g + i, 64) * part[i];
+      const int j0 = t0 + 16 * (gb + u) + 4 * g;
+      if (i16 == 0) {
+        if (j0 + 3 < n_local && (reinterpret_cast<uintptr_t>(out_row + j0) & 15u) == 0) {
+          *reinterpret_cast<f32x4*>(out_row + j0) = res;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (j0 + i < n_local) out_row[j0 + i] = res[i];
+        }
+      }
     }
   }
 }
@@ -277,7 +285,249 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(TopkParams 
   }
 }
 
+// Local top-k of lists of at most kLocalFastMax scores, held in registers
+// (32 per thread): radix select on the 32-bit order image of the score (four
+// 8-bit digits, stopping early when a digit's bucket is taken whole), the
+// tied scores at the threshold taken by position, then the k keys sorted.
+// Histogram updates are combined per wave when a wave's values share a
+// bucket (the leading digits of nearby scores usually do).
+constexpr int kLocalVpt = 32;
+constexpr int kLocalFastMax = kSelectThreads * kLocalVpt;   // 32768
+
+__device__ __forceinline__ void hist_add(unsigned* hist, unsigned bin, bool on) {
+  const unsigned lead = __builtin_amdgcn_readfirstlane(on ? bin : 0xffffffffu);
+  const unsigned long long same = __ballot(on && bin == lead);
+  const int n_same = __popcll(same);
+  if (n_same >= 8) {
+    if (on && bin == lead) {
+      const unsigned long long lower = same & ((1ull << (threadIdx.x & 63)) - 1ull);
+      if (lower == 0ull) atomicAdd(&hist[bin], (unsigned)n_same);
+    } else if (on) {
+      atomicAdd(&hist[bin], 1u);
+    }
+  } else if (on) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
+__global__ __launch_bounds__(kSelectThreads) void topk_local_fast_kernel(TopkParams p) {
+  __shared__ unsigned hist[256];
+  __shared__ unsigned s_word[4];
+  __shared__ unsigned wave_sum[kSelectThreads / 64];
+  __shared__ unsigned long long sel[kMaxTopk];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const long long list = blockIdx.x;
+  const int shard = (int)(list / p.rows);
+  const long long row = list - (long long)shard * p.rows;
+  const int n = min(max(p.local_len[(long long)shard * p.rows + row], 0), p.max_local);
+  const int k = p.k;
+  const float* src = p.in_score + list * p.max_local;
+  unsigned key[kLocalVpt];
+#pragma unroll
+  for (int i = 0; i < kLocalVpt; ++i) {
+    const int e = tid + i * kSelectThreads;
+    const float v = e < n ? src[e] : 0.f;
+    key[i] = score_bits(v == 0.f ? 0.f : v);
+  }
+  const unsigned m = (unsigned)min(n, k);
+  unsigned thresh = 0u;         // select keys above thresh, and `need` keys equal to it
+  unsigned need = 0u;
+  bool ties = false;
+  if (n > k) {
+    unsigned prefix = 0u, mask = 0u, rem = (unsigned)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kLocalVpt; ++i) {
+        const int e = tid + i * kSelectThreads;
+        hist_add(hist, (key[i] >> shift) & 255u, e < n && (key[i] & mask) == prefix);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned above = 0u;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (above + hist[d] >= rem) break;
+          above += hist[d];
+        }
+        s_word[0] = prefix | ((unsigned)d << shift);
+        s_word[1] = rem - above;              // still to take from bucket d
+        s_word[2] = hist[d];                  // bucket d's size
+      }
+      __syncthreads();
+      prefix = s_word[0];
+      rem = s_word[1];
+      mask |= 255u << shift;
+      if (s_word[2] == rem) {                 // bucket d is taken whole
+        thresh = prefix;                      // every key >= prefix (its low bits are 0)
+        need = 0u;
+        ties = false;
+        break;
+      }
+      if (shift == 0) {                       // prefix is the k-th key's score image
+        thresh = prefix;
+        need = rem;
+        ties = true;
+      }
+      __syncthreads();
+    }
+  }
+  // ---- gather: keys above the threshold, and (ties) the first `need` keys
+  // equal to it by position (element order), with their 64-bit keys
+  if (tid == 0) s_word[3] = 0u;
+  __syncthreads();
+  unsigned base = 0u;
+#pragma unroll
+  for (int i = 0; i < kLocalVpt; ++i) {
+    const int e = tid + i * kSelectThreads;
+    const bool valid = e < n;
+    const bool above = valid && (ties ? key[i] > thresh : key[i] >= thresh);
+    bool take = above;
+    if (ties) {
+      // rank of this tie among the ties of round i, in element order
+      const bool tie = valid && key[i] == thresh;
+      const unsigned long long bal = __ballot(tie);
+      const unsigned before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_sum[wv] = __popcll(bal);
+      __syncthreads();
+      unsigned wbase = 0u, total = 0u;
+      for (int w = 0; w < kSelectThreads / 64; ++w) {
+        const unsigned c = wave_sum[w];
+        if (w < wv) wbase += c;
+        total += c;
+      }
+      take = above || (tie && base + wbase + before < need);
+      base += total;
+      __syncthreads();
+    }
+    if (take) {
+      const unsigned at = atomicAdd(&s_word[3], 1u);
+      if (at < m)
+        sel[at] = ((unsigned long long)key[i] << 32) |
+                  (unsigned)(0xffffffffu - (unsigned)(e * p.num_shards + shard));
+    }
+  }
+  __syncthreads();
+  int np2 = 1;
+  while (np2 < (int)m) np2 <<= 1;
+  for (int i = (int)m + tid; i < np2; i += kSelectThreads) sel[i] = 0ull;
+  __syncthreads();
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < np2 / 2; i += kSelectThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const unsigned long long a = sel[lo], c = sel[hi];
+        if ((a < c) == desc) {
+          sel[lo] = c;
+          sel[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += kSelectThreads) {
+    float sc = kNegInf;
+    int pos = -1;
+    if (i < (int)m) {
+      const unsigned long long kv = sel[i];
+      sc = bits_score((unsigned)(kv >> 32));
+      pos = (int)(0xffffffffu - (unsigned)(kv & 0xffffffffull));
+    }
+    p.out_score[list * k + i] = sc;
+    p.out_pos[list * k + i] = pos;
+  }
+}
+
+// Merge of sorted candidate lists by rank: the lists of a row (each in
+// selection order, padding last) are staged in LDS as keys; an element's
+// place in the merged order is its index in its own list plus, for every
+// other list, the number of that list's keys above it (a binary search; keys
+// are distinct).  Elements whose place is below k are written there.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeMaxKeys = 8192;                 // num_shards * k staged in LDS
+constexpr int kMergeRun = kMergeMaxKeys / kMergeThreads;   // consecutive elements per thread
+
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_rank_kernel(TopkParams p) {
+  __shared__ unsigned long long keys[kMergeMaxKeys];
+  __shared__ int s_valid;
+  const int tid = threadIdx.x;
+  const long long row = blockIdx.x;
+  const int K = p.k_in, N = p.num_shards, k = p.k;
+  if (tid == 0) s_valid = 0;
+  __syncthreads();
+  int valid = 0;
+  for (int e = tid; e < N * K; e += kMergeThreads) {
+    const int r = e / K, idx = e - r * K;
+    const long long at = ((long long)r * p.rows + row) * K + idx;
+    const int pos = p.in_pos[at];
+    const unsigned long long kv = pos >= 0 ? make_key(p.in_score[at], pos) : 0ull;
+    keys[e] = kv;
+    valid += kv != 0ull;
+  }
+  atomicAdd(&s_valid, valid);
+  __syncthreads();
+  const int m = min(s_valid, k);
+  // Each thread takes kMergeRun consecutive elements of one list (descending
+  // keys): the first one's count in every other list by binary search, the
+  // next ones by walking on from the previous count (counts only grow).
+  const int e0 = tid * kMergeRun;
+  int cnt[kMaxShards];
+  for (int e = e0; e < min(e0 + kMergeRun, N * K); ++e) {
+    const unsigned long long kv = keys[e];
+    if (kv == 0ull) break;                          // padding: the rest of the run too
+    const int r = e / K;
+    int place = e - r * K;
+    for (int o = 0; o < N; ++o) {
+      if (o == r) continue;
+      const unsigned long long* lst = keys + o * K;
+      int c;
+      if (e == e0 || (e % K) == 0) {
+        int lo = 0, hi = K;
+        while (lo < hi) {                           // first index whose key is below kv
+          const int mid = (lo + hi) >> 1;
+          if (lst[mid] > kv) lo = mid + 1;
+          else hi = mid;
+        }
+        c = lo;
+      } else {
+        c = cnt[o];
+        while (c < K && lst[c] > kv) ++c;
+      }
+      cnt[o] = c;
+      place += c;
+    }
+    if (place < k) {
+      const float sc = bits_score((unsigned)(kv >> 32));
+      const int pos = (int)(0xffffffffu - (unsigned)(kv & 0xffffffffull));
+      if (p.out_score) p.out_score[row * k + place] = sc;
+      if (p.out_pos) p.out_pos[row * k + place] = pos;
+      if (p.out_slot) {
+        const long long span = (long long)p.page_size * p.num_shards;
+        const long long lp = min((long long)pos / span, (long long)p.max_pages - 1);
+        p.out_slot[row * k + place] = (int)((long long)p.block_table[row * p.max_pages + lp] * span + pos % span);
+      }
+    }
+  }
+  for (int i = m + tid; i < k; i += kMergeThreads) {
+    if (p.out_score) p.out_score[row * k + i] = kNegInf;
+    if (p.out_pos) p.out_pos[row * k + i] = -1;
+    if (p.out_slot) p.out_slot[row * k + i] = -1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_topk_merge(const TopkParams& p, long long rows, hipStream_t stream) {
+  void* args[] = {(void*)&p};
+  if ((long long)p.num_shards * p.k_in > kMergeMaxKeys)
+    return hipLaunchKernel((const void*)topk_select_kernel, dim3((unsigned)rows), dim3(kSelectThreads),
+                           args, 0, stream);
+  return hipLaunchKernel((const void*)topk_merge_rank_kernel, dim3((unsigned)rows), dim3(kMergeThreads),
+                         args, 0, stream);
+}
 
 hipError_t launch_index_score(const IndexScoreParams& p, hipStream_t stream) {
   const long long blocks = p.rows * p.num_shards * (long long)p.tiles_per_list;
@@ -288,8 +538,9 @@ hipError_t launch_index_score(const IndexScoreParams& p, hipStream_t stream) {
 
 hipError_t launch_topk_select(const TopkParams& p, long long lists, hipStream_t stream) {
   void* args[] = {(void*)&p};
-  return hipLaunchKernel((const void*)topk_select_kernel, dim3((unsigned)lists), dim3(kSelectThreads),
-                         args, 0, stream);
+  const void* fn = (!p.merge && p.max_local <= kLocalFastMax) ? (const void*)topk_local_fast_kernel
+                                                              : (const void*)topk_select_kernel;
+  return hipLaunchKernel(fn, dim3((unsigned)lists), dim3(kSelectThreads), args, 0, stream);
 }
 
 int index_score_tokens_per_block() { return kScoreTokens; }

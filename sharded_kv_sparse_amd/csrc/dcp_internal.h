@@ -169,6 +169,7 @@ hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, hipStream_t stream)
 
 hipError_t launch_index_score(const IndexScoreParams& p, hipStream_t stream);
 hipError_t launch_topk_select(const TopkParams& p, long long lists, hipStream_t stream);
+hipError_t launch_topk_merge(const TopkParams& p, long long rows, hipStream_t stream);
 int index_score_tokens_per_block();
 hipError_t launch_gather_prefix(const GatherParams& p, bool fp8, int max_len, hipStream_t stream);
 hipError_t launch_merge_into(void* o_acc, float* lse_acc, const float* o_new, const float* lse_new,
