@@ -78,7 +78,7 @@ WorkspacePlan plan_workspace(long long rows, int heads, int num_shards, int spli
   size_t off = 0;
   w.cnt_row_off = off;
   const size_t hb = (size_t)(heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
-  if (want_merged) off += 2 * sizeof(int) * (size_t)rows * hb;      // per (row, head block)
+  if (want_merged) off += 4 * sizeof(int) * (size_t)rows * hb;      // per (row, head block)
   w.cnt_shard_off = off;
   if (want_partials && splits > 1) off += sizeof(int) * (size_t)rows * num_shards * hb;
   off = align256(off);

@@ -39,7 +39,7 @@
 
 namespace dcp {
 
-constexpr int kMaxWaitMembers = 24;         // abandon bits 8..31 of the arrival word
+constexpr int kMaxWaitMembers = 56;         // abandon bits 8..63 of the 64-bit arrival word
 
 // Weights of the n_in partials of a head block, from their LSEs: w[i][hl]
 // (normalised), and the merged LSE of each head written to out_lse when
@@ -435,6 +435,7 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   __syncthreads();       // ... and so have those of every thread of the block
   DCP_LDS float* w = (DCP_LDS float*)smem;                    // [kMaxMergeInputs][64]
   DCP_LDS unsigned* s_word = (DCP_LDS unsigned*)(w + kMaxMergeInputs * kHeadsPerBlock);
+  DCP_LDS unsigned long long* s_seen = (DCP_LDS unsigned long long*)(s_word + 2);  // arrival word read
   DCP_LDS int* wx = (DCP_LDS int*)(s_word + 64);              // [kMaxMergeInputs][64]
 
   if (need_shard_merge) {
@@ -455,17 +456,18 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   }
   if (!fused) return;
 
-  // ---- all partials of the row -> o.  Arrival word: count in bits 0..7,
-  // abandoned parts in bits 8 + member.  Completion word: parts merged.
-  unsigned* arrive = reinterpret_cast<unsigned*>(p.cnt_row + (row * HB + hblk) * 2);
-  unsigned* done = arrive + 1;
+  // ---- all partials of the row -> o.  Arrival word (64 bits): count in
+  // bits 0..7, abandoned parts in bits 8 + member.  Completion word: parts
+  // merged.  Four 32-bit counter words per (row, head block).
+  unsigned long long* arrive = reinterpret_cast<unsigned long long*>(p.cnt_row + (row * HB + hblk) * 4);
+  unsigned* done = reinterpret_cast<unsigned*>(p.cnt_row + (row * HB + hblk) * 4 + 2);
   // Abandons this block's part: with an own part kept in registers, that
   // part is stored (and waited for) first.  Returns the parts to merge.
-  auto give_up = [&](unsigned now) -> unsigned {
+  auto give_up = [&](unsigned long long now) -> unsigned {
     for (;;) {
-      if ((now & 0xffu) == (unsigned)n_in) return 1u;
-      unsigned expect = now;
-      if (__hip_atomic_compare_exchange_strong(arrive, &expect, now | (1u << (8 + member)),
+      if ((now & 0xffull) == (unsigned long long)n_in) return 1u;
+      unsigned long long expect = now;
+      if (__hip_atomic_compare_exchange_strong(arrive, &expect, now | (1ull << (8 + member)),
                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT))
         return 0u;                       // abandoned: the last arriver merges this part
@@ -473,21 +475,24 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
     }
   };
   if (tid == 0) {
-    const unsigned add = 1u + (!may_wait && n_in <= kMaxWaitMembers ? 1u << (8 + member) : 0u);
-    const unsigned old = __hip_atomic_fetch_add(arrive, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long add =
+        1ull + (!may_wait && n_in <= kMaxWaitMembers ? 1ull << (8 + member) : 0ull);
+    const unsigned long long old =
+        __hip_atomic_fetch_add(arrive, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned parts = 0u;                 // bit 0: own part; bit 1: last arriver
-    if ((old & 0xffu) == (unsigned)n_in - 1) {
+    if ((old & 0xffull) == (unsigned long long)n_in - 1) {
       parts = 3u;
-      s_word[1] = old;
+      *s_seen = old;
     } else if (may_wait) {
       const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
       for (;;) {
-        const unsigned now = __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((now & 0xffu) == (unsigned)n_in) { parts = 1u; break; }
+        const unsigned long long now =
+            __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((now & 0xffull) == (unsigned long long)n_in) { parts = 1u; break; }
         if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)p.merge_wait_ticks) {
           if (own) {
             parts = 4u;                  // timed out: store the own part first
-            s_word[1] = now;
+            *s_seen = now;
           } else {
             parts = give_up(now);
           }
@@ -509,7 +514,7 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
     }
     wait_vmcnt<0>();
     __syncthreads();
-    if (tid == 0) s_word[0] = give_up(s_word[1]);
+    if (tid == 0) s_word[0] = give_up(*s_seen);
     __syncthreads();
     parts = s_word[0];
   }
@@ -517,7 +522,7 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   // The last arriver merges every part whose member gave up (all parts
   // when there are too many members for abandon bits).
   const bool all = (parts & 2u) && n_in > kMaxWaitMembers;
-  const unsigned abandoned = (parts & 2u) ? (s_word[1] >> 8) : 0u;
+  const unsigned long long abandoned = (parts & 2u) ? (*s_seen >> 8) : 0ull;
 
   void* out = p.out_bf16 ? (void*)(static_cast<unsigned short*>(p.o) + row * H * kVDim)
                          : (void*)(static_cast<float*>(p.o) + row * H * kVDim);
@@ -534,7 +539,7 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   }
   for (int m = 0; m < n_in; ++m) {
     if (own && m == member) continue;
-    if (!(all || m == member || (m < kMaxWaitMembers && ((abandoned >> m) & 1u)))) continue;
+    if (!(all || m == member || (m < kMaxWaitMembers && ((abandoned >> m) & 1ull)))) continue;
     if (half_ws) merge_part<NT, true>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
     else merge_part<NT, false>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
     ++merged;
@@ -544,7 +549,7 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
     const unsigned prev =
         __hip_atomic_fetch_add(done, (unsigned)merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev + (unsigned)merged == (unsigned)n_in) {
-      __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(arrive, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

@@ -175,12 +175,15 @@ def test_sparse_decode_splits(gpu, kv, splits):
     check_against_oracle(res, oracle_sparse(w), f"splits={splits}")
 
 
-@pytest.mark.parametrize("kv,splits", [("fp8", 8), ("fp8", 12), ("fp8", 32), ("bf16", 32)])
+@pytest.mark.parametrize("kv,splits", [("fp8", 8), ("fp8", 12), ("fp8", 20), ("fp8", 32),
+                                       ("bf16", 32)])
 def test_sparse_decode_many_partials(gpu, kv, splits):
-    # 16, 24 or 64 partials per row (2 shards x splits): the merge's wide load
-    # groups (16 or 32 members per pass, several groups), two rounds of LSE
-    # loads, rows merged by their last block alone (more than 24 partials),
-    # and empty splits; merged and per-shard outputs within tolerance
+    # 16, 24, 40 or 64 partials per row (2 shards x splits): the merge's wide
+    # load groups (16 or 32 members per pass, several groups), two rounds of
+    # LSE loads, abandon bits above bit 31 of the arrival word (40 members
+    # merging in parallel), rows merged by their last block alone (64
+    # partials, more than the 56 abandon bits), and empty splits; merged and
+    # per-shard outputs within tolerance
     p = wl.Preset("t", "sparse", kv, batch=2, q_per_seq=1, heads=64, context=40000, num_shards=2,
                   topk=8000, pad_tail=300, seed=60 + splits)
     w = make(p)
