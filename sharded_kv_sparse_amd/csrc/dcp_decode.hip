@@ -20,9 +20,12 @@
 // Inside a block, wave w owns 16 heads (head group hg) and, when the block
 // has fewer than four head groups, a share of each tile's tokens (token
 // group ts).  Per tile:
-//   * the KV rows of T tokens (T = 64 FP8 / 32 BF16: 36 KB either way) are
-//     copied straight from HBM into LDS with global->LDS DMA, three stages
-//     deep, rows stored 16-byte-chunk-swizzled against bank conflicts;
+//   * the KV rows of 64 tokens (36 KB FP8, three stages; 72 KB BF16, two
+//     stages) are copied straight from HBM into LDS with global->LDS DMA,
+//     granule-major (each copy instruction moves one 64-byte granule of 16
+//     tokens, so a lane keeps one token, and one id, for all its copies of
+//     a tile), chunks swizzled against bank conflicts; the tile's slot or
+//     page ids arrive two tiles ahead in an LDS ring, by the same DMA;
 //   * S^T = K Q^T on bf16 MFMA 16x16x32 (K codes converted to bf16 after the
 //     LDS read -- E4M3 is exact in bf16; Q stays in registers for the block);
 //   * online softmax in base 2, row statistics kept per head = per lane
@@ -42,49 +45,77 @@
 namespace dcp {
 namespace {
 
+// Tiles are stored granule-major: [granule G (64 bytes of the row)][token t]
+// [4 x 16-byte chunks], the chunks of token t permuted by XOR with
+// chunk_sw(t), which keeps the 16-byte operand reads of S^T = K Q^T free of
+// bank conflicts.  FP8: 64-token tiles of 9 granules (576-byte rows) plus the
+// tile's 64 fp32 token scales; BF16: 32-token tiles of 18 granules
+// (1,152-byte rows).  36 KB either way, four stages: one tile computed while
+// the next three are in flight.
 template <bool FP8> struct Tile;
 template <> struct Tile<true> {
-  static constexpr int T = 64;       // tokens per tile
-  static constexpr int RB = 576;     // bytes per KV row
-  static constexpr int CPR = 36;     // 16-byte chunks per row
+  static constexpr int T = 64;         // tokens per tile
+  static constexpr int GR = 9;         // granules per row
+  static constexpr int SCALE_BYTES = 256;
 };
 template <> struct Tile<false> {
   static constexpr int T = 32;
-  static constexpr int RB = 1152;
-  static constexpr int CPR = 72;
+  static constexpr int GR = 18;
+  static constexpr int SCALE_BYTES = 0;
 };
+constexpr int kStages = 4;
+// The ids of a tile enter the ring kIdsAhead tiles before its rows are
+// copied; kRingSlots covers every tile whose ids are in flight or in use.
+constexpr int kIdsAhead = kStages - 2;
+constexpr int kRingSlots = kStages + kIdsAhead;
 
-// Chunk swizzle of token t's row: logical chunk c sits at position c ^ swz(t).
-// The XOR stays inside an aligned group of 4 (FP8) or 8 (BF16) chunks, and
-// 36 and 72 are multiples of those.
-template <bool FP8>
-__device__ __forceinline__ int swz(int t) {
-  if constexpr (FP8) return ((t >> 2) ^ (t >> 4)) & 3;
-  else return (t >> 1) & 7;
-}
+// Chunk permutation of token t inside its 64-byte granule.
+__device__ __forceinline__ int chunk_sw(int t) { return ((t >> 1) ^ (t >> 3) ^ (t >> 4)) & 3; }
 
-constexpr int kTileBytes = 36864;
-constexpr int kStages = 3;
-constexpr int kStageBytes = kTileBytes + 256;            // + 64 fp32 scales (FP8)
-constexpr int kListOff = kStages * kStageBytes;
-constexpr int kSmemBytes = kListOff + kMaxList * 4;
+// The page table of a prefill chunk: one page, id 0, holding the whole chunk.
+__device__ int kChunkPageId[1] = {0};
 
 template <bool FP8, bool DENSE, int NW, int TS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const DecodeParams p) {
   using TL = Tile<FP8>;
-  constexpr int T = TL::T, RB = TL::RB, CPR = TL::CPR;
+  constexpr int T = TL::T, GR = TL::GR;
+  constexpr int kPlane = T * 64;                   // bytes of one granule plane of a tile
+  constexpr int kTileBytes = GR * kPlane;
+  constexpr int kStageBytes = kTileBytes + TL::SCALE_BYTES;
+  constexpr int kRingOff = kStages * kStageBytes;
+  constexpr int kSmemBytes = kRingOff + kRingSlots * 64 * 4;
   constexpr int NT = NW * 64;
   constexpr int HG = NW / TS;          // head groups of 16 in this block
   constexpr int TSUB = T / TS;         // tokens of a tile per token group
-  constexpr int NKB = TSUB / 32;       // 32-token PV blocks per wave per tile
-  constexpr int IPW = (kTileBytes / 1024) / NW;   // DMA instructions per wave per tile
-  static_assert(NKB >= 1 && IPW * NW * 1024 == kTileBytes, "tile split");
+  constexpr int CT = TSUB >= 32 ? 32 : 16;   // tokens per softmax / PV chunk
+  constexpr int CST = CT / 16;         // 16-token S tiles per chunk
+  constexpr int NKB = TSUB / CT;       // chunks per wave per tile
+  // Row copies: TGT groups of 16 tokens per tile; a wave copies whole token
+  // groups (TGW of them) or, with more waves than groups, every WPT-th
+  // granule of one group.
+  constexpr int TGT = T / 16;
+  constexpr int TGW = TGT >= NW ? TGT / NW : 1;
+  constexpr int WPT = NW >= TGT ? NW / TGT : 1;
+  constexpr int IPW = TGW * GR / WPT;  // row copies per wave per tile
+  constexpr int kRingWave = NW - 1;    // copies each tile's ids into the ring
+  static_assert(NKB >= 1 && GR % WPT == 0 && NW * IPW == TGT * GR && (TGT % NW == 0 || NW % TGT == 0),
+                "tile split");
+  static_assert(!FP8 || CT == 32, "FP8 chunks are 32 tokens");
+  static_assert(NW > 1, "the ring wave is not wave 0");
+  static_assert((TS - 1) * HG * 64 * 130 * 4 <= kRingOff, "token-group merge space");
+  static_assert(kMaxMergeInputs * kHeadsPerBlock * 8 + 256 <= kRingOff, "merge space");
+  // vector-memory operations a wave queues per tile (rows; FP8 wave 0 also
+  // the scales), and what may stay in flight at the top of a tile in steady
+  // state: the rows of the next kStages - 2 tiles (and for the ring wave the
+  // ids queued between them)
+  constexpr int kOps0 = IPW + (FP8 ? 1 : 0), kOps = IPW;
+  static_assert((kStages - 2) * kOps0 + kIdsAhead - 1 < 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
   __shared__ int s_flag;
   DCP_LDS char* smem = (DCP_LDS char*)smem_raw;
-  DCP_LDS int* list = (DCP_LDS int*)(smem + kListOff);
+  DCP_LDS int* ring = (DCP_LDS int*)(smem + kRingOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,36 +151,70 @@ void decode_kernel(const DecodeParams p) {
     n_tok = min(p.counts[(long long)shard * p.rows + row], p.k);
   }
   n_tok = max(n_tok, 0);
-  const int chunk = ((n_tok + S - 1) / S + T - 1) / T * T;
+  const int chunk = ((n_tok + S - 1) / S + 63) / 64 * 64;
   const int start = min(n_tok, split * chunk);
   const int end = min(n_tok, start + chunk);
   const int ntiles = (end - start + T - 1) / T;
 
-  // ---- stage the block's slot ids (sparse) or page ids (dense) in LDS
+  // ---- ids.  Local token j's id is its compacted slot id (sparse) or the id
+  // of its logical page (dense).  A tile's ids are copied into a ring slot of
+  // LDS by global->LDS DMA (one 4-byte copy per token) kIdsAhead tiles before
+  // its rows, so that the row copies need no dependent global load.  Tokens
+  // past a tile's valid count stand in for its first token: they are masked
+  // out of the softmax, and a real row keeps their V values finite.
   const int page = DENSE ? p.page_size : 1;
-  const int pg0 = DENSE ? start / page : 0;
-  if constexpr (DENSE) {
-    const int npg = end > start ? (end - 1) / page - pg0 + 1 : 0;
-    // (a prefill chunk is one page, id 0, holding the whole chunk)
-    const int* bt = p.chunk_mode ? nullptr : p.block_table + row * p.max_pages + pg0;
-    for (int i = tid; i < min(npg, kMaxList); i += NT) list[i] = p.chunk_mode ? 0 : bt[i];
-  } else {
-    const int* src = p.topk_local + ((long long)shard * p.rows + row) * p.k + start;
-    for (int i = tid; i < min(end - start, kMaxList); i += NT) list[i] = src[i];
-  }
-
-  // Pool row of local token j (start <= j < end), clamped into the pool.
-  auto pool_row = [&](int j) -> long long {
-    long long r;
-    if constexpr (DENSE) {
-      const int pg = j / page;
-      const int li = min(max(pg - pg0, 0), kMaxList - 1);
-      r = (long long)list[li] * page + (j - pg * page);
-    } else {
-      r = list[min(max(j - start, 0), kMaxList - 1)];
-    }
+  const int* ids = DENSE ? (p.chunk_mode ? kChunkPageId : p.block_table + row * p.max_pages)
+                         : p.topk_local + ((long long)shard * p.rows + row) * p.k;
+  auto tile_tok0 = [&](int it) { return start + it * T; };
+  auto eff = [&](int it, int t) { return t < end - tile_tok0(it) ? t : 0; };
+  auto pool_row = [&](int j, int id) -> long long {
+    const long long r = DENSE ? (long long)id * page + (j - (j / page) * page) : (long long)id;
     return min(max(r, 0LL), max_prow);
   };
+  // (wave kRingWave) ids of tile `it` into its ring slot; a tile past the
+  // last one copies the last tile's ids (never read), so that every tile
+  // queues the same operations
+  auto issue_ring = [&](int it) {
+    const int src_it = min(it, ntiles - 1);
+    const int j = tile_tok0(src_it) + eff(src_it, lane);
+    dma4(DENSE ? ids + j / page : ids + j, ring + (it % kRingSlots) * 64);
+  };
+  // Rows of tile `it` into its stage, its ids already in the ring: lane l of
+  // a copy covers token 16 tg + l / 4 of the tile and the 16-byte chunk
+  // (l & 3) ^ chunk_sw of a granule of its row.  Wave 0 also copies the
+  // tile's 64 fp32 scales (FP8).
+  auto issue_tile = [&](int it) {
+    DCP_LDS char* sb = smem + (it % kStages) * kStageBytes;
+    const DCP_LDS int* rg = ring + (it % kRingSlots) * 64;
+    const int tok0 = tile_tok0(it);
+#pragma unroll
+    for (int jg = 0; jg < TGW; ++jg) {
+      const int tg = TGT >= NW ? wave * TGW + jg : wave % TGT;
+      const int t = 16 * tg + (lane >> 2);
+      const int te = eff(it, t);
+      const char* src = kvbase + pool_row(tok0 + te, rg[te]) * sh.row_stride +
+                        16 * ((lane & 3) ^ chunk_sw(t));
+#pragma unroll
+      for (int k = 0; k < GR / WPT; ++k) {
+        const int G = TGT >= NW ? k : wave / TGT + WPT * k;
+        dma16(src + 64 * G, sb + G * kPlane + tg * 1024);
+      }
+    }
+    if constexpr (FP8) {
+      if (wave == 0) {
+        const int te = eff(it, lane);
+        dma4(reinterpret_cast<const float*>(reinterpret_cast<const char*>(sh.scale) +
+                                            pool_row(tok0 + te, rg[te]) * sh.scale_stride),
+             sb + kTileBytes);
+      }
+    }
+  };
+  // ids of the tiles whose rows are copied before the loop or in its first
+  // kIdsAhead iterations
+  if (wave == kRingWave && ntiles > 0) {
+#pragma unroll
+    for (int it = 0; it < kStages - 1 + kIdsAhead; ++it) issue_ring(it);
+  }
 
   // ---- query fragments (B operand of S^T = K Q^T), kept for the whole block.
   // BF16 KV: bf16 Q on the bf16 MFMA; k-step s covers dims 32s..32s+31 and
@@ -211,35 +276,16 @@ void decode_kernel(const DecodeParams p) {
   } else {
 #pragma unroll
     for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g);
-    // Complete the query loads here, so that no wait for them lands inside
-    // the tile loop (where it would also drain the in-flight KV copies).
 #pragma unroll
     for (int s = 0; s < 18; ++s) touch(qf[s]);
   }
-  __syncthreads();   // list visible
 
-  auto issue_tile = [&](int it) {
-    DCP_LDS char* sbase = smem + (it % kStages) * kStageBytes;
-    const int tok0 = start + it * T;
-    const int nval = min(T, end - tok0);
-#pragma unroll 3
-    for (int ii = 0; ii < IPW; ++ii) {
-      const int blk = wave * IPW + ii;
-      const int lc = blk * 64 + lane;
-      const int t = lc / CPR;
-      const int pch = lc - t * CPR;
-      const long long prow = pool_row(tok0 + (t < nval ? t : 0));
-      const int c = pch ^ swz<FP8>(t);
-      dma16(kvbase + prow * sh.row_stride + c * 16, sbase + blk * 1024);
-    }
-    if constexpr (FP8) {
-      if (wave == 0) {
-        const long long prow = pool_row(tok0 + (lane < nval ? lane : 0));
-        dma4(reinterpret_cast<const float*>(reinterpret_cast<const char*>(sh.scale) + prow * sh.scale_stride),
-             sbase + kTileBytes);
-      }
-    }
-  };
+  // ---- the first tiles' ids are in the ring: copy their rows
+  wait_vmcnt<0>();
+  lds_barrier();
+#pragma unroll
+  for (int it = 0; it < kStages - 1; ++it)
+    if (it < ntiles) issue_tile(it);
 
   // ---- online-softmax state: per lane, head = hg*16 + i16; O^T tiles
   float m_run = kNegInf;    // reference max (base-2 logits), see the softmax below
@@ -254,44 +300,49 @@ void decode_kernel(const DecodeParams p) {
   constexpr int kNoExp = 1000;
   [[maybe_unused]] int pe_run = kNoExp;
 
-  for (int it = 0; it < kStages - 1 && it < ntiles; ++it) issue_tile(it);
-
   for (int it = 0; it < ntiles; ++it) {
-    // Tile `it` has landed once at most one later tile's copies are in flight.
-    if (it + 1 < ntiles) {
-      if (FP8 && wave == 0) wait_vmcnt<IPW + 1>();
-      else wait_vmcnt<IPW>();
+    // Tile `it` (and the ids of tile it + kStages - 1) have landed once at
+    // most the rows of tiles it + 1 .. it + kStages - 2 (and, for the ring
+    // wave after the first tile, the ids queued between them) are in flight.
+    if (it + kStages - 2 < ntiles) {
+      if (wave == 0) wait_vmcnt<(kStages - 2) * kOps0>();
+      else if (wave == kRingWave && it > 0) wait_vmcnt<(kStages - 2) * kOps + kIdsAhead - 1>();
+      else wait_vmcnt<(kStages - 2) * kOps>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();
+    if (wave == kRingWave) issue_ring(it + kStages - 1 + kIdsAhead);
     if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1);
 
     const DCP_LDS char* sbase = smem + (it % kStages) * kStageBytes;
-    const int tok0 = start + it * T;
+    const int tok0 = tile_tok0(it);
 
-    // The wave's share of the tile in 32-token chunks: S^T for two 16-token
-    // S tiles, the softmax update, then O^T += V^T P^T for those 32 tokens.
+    // The wave's share of the tile in chunks of CT tokens: S^T for the
+    // chunk's 16-token S tiles, the softmax update, then O^T += V^T P^T.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int sub0 = ts * TSUB + 32 * kb;
-      constexpr int CST = 2;   // S tiles per chunk
+      const int sub0 = ts * TSUB + CT * kb;
 
-      // S^T = K Q^T; the two S tiles are independent accumulators,
-      // interleaved so back-to-back MFMAs never wait on each other.  The
-      // operands of k-step s+1 are read from LDS while step s multiplies.
-      f32x4 sacc[CST];
+      // S^T = K Q^T; two independent accumulators, interleaved so that
+      // back-to-back MFMAs never wait on each other (the chunk's two S tiles,
+      // or a 16-token chunk's even and odd k-steps).  The operands of k-step
+      // s + 1 (FP8) or s + 2 (BF16) are read from LDS while step s multiplies.
+      f32x4 sacc[2];
 #pragma unroll
-      for (int st = 0; st < CST; ++st) sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < 2; ++st) sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (FP8) {
+        // k-step s, lane group g: dims 128s + 32g .. +32 = chunks 2(g & 1),
+        // 2(g & 1) + 1 of granule 2s + (g >> 1) (dims >= 576 are padding)
         auto load_k = [&](int s, i32x8* a) {
-          const bool live = (s < 4) || (g < 2);     // dims 576..639 are padding
-          const int c0 = live ? 8 * s + 2 * g : 0;
+          const bool live = (s < 4) || (g < 2);
+          const int G = live ? 2 * s + (g >> 1) : 0;
+          const int c0 = 2 * (g & 1);
 #pragma unroll
           for (int st = 0; st < CST; ++st) {
             const int t = sub0 + st * 16 + i16;
-            const DCP_LDS char* rp = sbase + t * RB;
-            const int sw = swz<FP8>(t);
+            const DCP_LDS char* rp = sbase + G * kPlane + t * 64;
+            const int sw = chunk_sw(t);
             const i32x4 lo4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp + 16 * (c0 ^ sw));
             const i32x4 hi4 = *reinterpret_cast<const DCP_LDS i32x4*>(rp + 16 * ((c0 + 1) ^ sw));
             a[st] = live ? i32x8{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w} : i32x8{};
@@ -313,12 +364,13 @@ void decode_kernel(const DecodeParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
+        // k-step s, lane group g: dims 32s + 8g .. +8 = chunk g of granule s
         auto load_k = [&](int s, bf16x8* a) {
 #pragma unroll
           for (int st = 0; st < CST; ++st) {
             const int t = sub0 + st * 16 + i16;
-            a[st] = *reinterpret_cast<const DCP_LDS bf16x8*>(
-                sbase + t * RB + 16 * ((4 * s + g) ^ swz<FP8>(t)));
+            a[st] = *reinterpret_cast<const DCP_LDS bf16x8*>(sbase + s * kPlane + t * 64 +
+                                                            16 * (g ^ chunk_sw(t)));
           }
         };
         bf16x8 a[3][CST];
@@ -327,18 +379,23 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
           if (s + 2 < 18) load_k(s + 2, a[(s + 2) % 3]);
+          if constexpr (CST == 2) {
 #pragma unroll
-          for (int st = 0; st < CST; ++st)
-            sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s % 3][st], qf[s], sacc[st], 0, 0, 0);
+            for (int st = 0; st < 2; ++st)
+              sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s % 3][st], qf[s], sacc[st], 0, 0, 0);
+          } else {
+            sacc[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s % 3][0], qf[s], sacc[s & 1], 0, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (CST == 1) sacc[0] += sacc[1];
       }
 
       // First V^T operands of the chunk, read before the softmax so their
       // LDS latency hides behind it (see the PV loop below for the layout).
       const int blk0 = sub0;
       [[maybe_unused]] i32x2 vraw[2][8];
-      [[maybe_unused]] i16x4 vr16[2][4][2];
+      [[maybe_unused]] i16x4 vr16[2][4][CST];
       [[maybe_unused]] const DCP_LDS char* vp = nullptr;
       [[maybe_unused]] int vsw = 0;
       [[maybe_unused]] const DCP_LDS char* va = nullptr;
@@ -347,31 +404,35 @@ void decode_kernel(const DecodeParams p) {
       if constexpr (FP8) {
         // tr8: lane i of a 16-lane group receives byte i%8 from the lanes
         // (i/8) + 2j; lane L therefore points at token slot L/2, bytes
-        // [16d + 8(L%2), +8) -- lane i ends up with dim 16d + i of 8 tokens.
+        // [16d + 8(L%2), +8) of the row (chunk d & 3 of granule d >> 2) --
+        // lane i ends up with dim 16d + i of 8 tokens.
         const int jj = i16 >> 1;
         const int tk = blk0 + (jj < 4 ? 4 * g + jj : 16 + 4 * g + (jj - 4));
-        vp = sbase + tk * RB + 8 * (i16 & 1);
-        vsw = swz<FP8>(tk);
+        vp = sbase + tk * 64 + 8 * (i16 & 1);
+        vsw = chunk_sw(tk);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          vraw[0][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DCP_LDS i32x2*)(vp + 16 * (j ^ vsw)));
+          vraw[0][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (DCP_LDS i32x2*)(vp + (j >> 2) * kPlane + 16 * ((j & 3) ^ vsw)));
       } else {
         // tr16: lane i receives element i%4 from the lanes (i/4) + 4j; lane L
-        // points at token slot L/4 (+4 for the second read), elements
-        // [16d + 4(L%4), +4) -- lane i ends up with dim 16d + i of 4 tokens.
+        // points at token slot L/4 (and 16 + L/4 for the second S tile),
+        // elements [16d + 4(L%4), +4) = bytes 32d + 8(L%4) of the row (chunk
+        // 2(d & 1) + (L%4)/2 of granule d >> 1) -- lane i ends up with dim
+        // 16d + i of 4 tokens.
         const int tka = blk0 + 4 * g + (i16 >> 2);
-        const int tkb = blk0 + 16 + 4 * g + (i16 >> 2);
-        swa = swz<FP8>(tka);
-        swb = swz<FP8>(tkb);
+        const int tkb = tka + 16;
+        swa = chunk_sw(tka);
+        swb = chunk_sw(tkb);
         vhalf = (i16 & 3) >> 1;
-        va = sbase + tka * RB + 8 * (i16 & 1);
-        vb = sbase + tkb * RB + 8 * (i16 & 1);
+        va = sbase + tka * 64 + 8 * (i16 & 1);
+        vb = sbase + tkb * 64 + 8 * (i16 & 1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vr16[0][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DCP_LDS i16x4*)(va + 16 * ((2 * j + vhalf) ^ swa)));
-          vr16[0][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DCP_LDS i16x4*)(vb + 16 * ((2 * j + vhalf) ^ swb)));
+          const int c = 2 * (j & 1) + vhalf, off = (j >> 1) * kPlane;
+          vr16[0][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DCP_LDS i16x4*)(va + off + 16 * (c ^ swa)));
+          if constexpr (CST == 2)
+            vr16[0][j][CST - 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DCP_LDS i16x4*)(vb + off + 16 * (c ^ swb)));
         }
       }
 
@@ -423,11 +484,14 @@ void decode_kernel(const DecodeParams p) {
         }
       }
 
-      // O^T += V^T P^T over the chunk's 32 tokens.  k-slot j of lane group g
-      // is token 4g+j (j < 4) or 16+4g+(j-4) (j >= 4) of the chunk: exactly
-      // the tokens this lane holds in the two S tiles, so P needs no shuffle.
-      // V^T operands are read in groups of 8 (FP8) / 4 (BF16) 16-dim tiles,
-      // one group ahead of the MFMAs that consume them.
+      // O^T += V^T P^T over the chunk.  32-token chunks: k-slot j of lane
+      // group g is token 4g+j (j < 4) or 16+4g+(j-4) (j >= 4) of the chunk,
+      // exactly the tokens this lane holds in the two S tiles, so P needs no
+      // shuffle.  16-token chunks (BF16): k-slots j < 4 carry P's bf16 hi
+      // part of token 4g+j and j >= 4 its lo part, against the V^T of token
+      // 4g+(j-4) read once and used twice.  V^T operands are read in groups
+      // of 8 (FP8) / 4 (BF16) 16-dim tiles, one group ahead of the MFMAs
+      // that consume them.
       if constexpr (FP8) {
         // The head's largest P' over its four lanes sets the power of two; a
         // larger P' than before lowers it, and O^T is scaled down to match
@@ -452,15 +516,15 @@ void decode_kernel(const DecodeParams p) {
         const float ps = pe_run != kNoExp ? pow2i(pe_run) : 1.0f;
         const f16x8 bp = f16x8{(_Float16)(pr[0][0] * ps), (_Float16)(pr[0][1] * ps),
                                (_Float16)(pr[0][2] * ps), (_Float16)(pr[0][3] * ps),
-                               (_Float16)(pr[1][0] * ps), (_Float16)(pr[1][1] * ps),
-                               (_Float16)(pr[1][2] * ps), (_Float16)(pr[1][3] * ps)};
+                               (_Float16)(pr[CST - 1][0] * ps), (_Float16)(pr[CST - 1][1] * ps),
+                               (_Float16)(pr[CST - 1][2] * ps), (_Float16)(pr[CST - 1][3] * ps)};
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           if (grp + 1 < 4) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
               vraw[(grp + 1) & 1][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                  (DCP_LDS i32x2*)(vp + 16 * ((8 * (grp + 1) + j) ^ vsw)));
+                  (DCP_LDS i32x2*)(vp + (2 * (grp + 1) + (j >> 2)) * kPlane + 16 * ((j & 3) ^ vsw)));
           }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -472,12 +536,22 @@ void decode_kernel(const DecodeParams p) {
         }
       } else {
         bf16x8 bh, bl;
+        if constexpr (CST == 2) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = pr[j >> 2][j & 3];
-          const __bf16 hi = f32_to_bf16(v);
-          bh[j] = hi;
-          bl[j] = f32_to_bf16(v - bf16_to_f32(hi));
+          for (int j = 0; j < 8; ++j) {
+            const float v = pr[(j >> 2) & (CST - 1)][j & 3];
+            const __bf16 hi = f32_to_bf16(v);
+            bh[j] = hi;
+            bl[j] = f32_to_bf16(v - bf16_to_f32(hi));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = pr[0][j];
+            const __bf16 hi = f32_to_bf16(v);
+            bh[j] = hi;
+            bh[4 + j] = f32_to_bf16(v - bf16_to_f32(hi));
+          }
         }
 #pragma unroll
         for (int grp = 0; grp < 8; ++grp) {
@@ -485,20 +559,22 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int d = 4 * (grp + 1) + j;
+              const int c = 2 * (d & 1) + vhalf, off = (d >> 1) * kPlane;
               vr16[(grp + 1) & 1][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (DCP_LDS i16x4*)(va + 16 * ((2 * d + vhalf) ^ swa)));
-              vr16[(grp + 1) & 1][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (DCP_LDS i16x4*)(vb + 16 * ((2 * d + vhalf) ^ swb)));
+                  (DCP_LDS i16x4*)(va + off + 16 * (c ^ swa)));
+              if constexpr (CST == 2)
+                vr16[(grp + 1) & 1][j][CST - 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (DCP_LDS i16x4*)(vb + off + 16 * (c ^ swb)));
             }
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int d = 4 * grp + j;
             const i32x2 ra2 = __builtin_bit_cast(i32x2, vr16[grp & 1][j][0]);
-            const i32x2 rb2 = __builtin_bit_cast(i32x2, vr16[grp & 1][j][1]);
+            const i32x2 rb2 = __builtin_bit_cast(i32x2, vr16[grp & 1][j][CST - 1]);
             const bf16x8 a = __builtin_bit_cast(bf16x8, i32x4{ra2.x, ra2.y, rb2.x, rb2.y});
             oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[d], 0, 0, 0);
-            oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, oacc[d], 0, 0, 0);
+            if constexpr (CST == 2) oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, oacc[d], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -563,17 +639,12 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
 template <bool FP8, bool DENSE>
 hipError_t launch_heads(const DecodeParams& p, hipStream_t stream) {
   // heads per block = min(H, 64): four 16-head groups, or fewer groups with
-  // the tile's tokens shared between waves (FP8 tiles hold two 32-token
-  // blocks; BF16 tiles one).
+  // each 64-token tile's two 32-token halves shared between waves.
   switch (p.heads) {
     case 128:
     case 64: return launch_one<FP8, DENSE, 4, 1>(p, stream);
-    case 32:
-      if constexpr (FP8) return launch_one<FP8, DENSE, 4, 2>(p, stream);
-      else return launch_one<FP8, DENSE, 2, 1>(p, stream);
-    case 16:
-      if constexpr (FP8) return launch_one<FP8, DENSE, 2, 2>(p, stream);
-      else return launch_one<FP8, DENSE, 1, 1>(p, stream);
+    case 32: return launch_one<FP8, DENSE, 4, 2>(p, stream);
+    case 16: return launch_one<FP8, DENSE, 2, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
