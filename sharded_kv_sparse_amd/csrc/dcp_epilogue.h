@@ -126,17 +126,22 @@ struct WsPartials {
   }
 };
 
-// Merges part `part` of `n_parts` of the head block's 128 * nh float4
-// elements (element e: dim tile e / 4nh, head (e / 4) % nh, lane group e % 4)
-// over the partials part0 .. part0 + n_in - 1 into out (the output row's
-// [H][512] values, fp32 or bf16).  Whole block.
+// Element range of parts [m0, m1) of n_parts of a head block's 128 * nh
+// float4 elements.
+__device__ __forceinline__ int2 part_range(int m0, int m1, int n_parts, int nh) {
+  const long long T = 128LL * nh;
+  return make_int2((int)(m0 * T / n_parts), (int)(m1 * T / n_parts));
+}
+
+// Merges the head block's float4 elements [e0, e1) (element e: dim tile
+// e / 4nh, head (e / 4) % nh, lane group e % 4) over the partials part0 ..
+// part0 + n_in - 1 into out (the output row's [H][512] values, fp32 or
+// bf16).  Whole block.
 template <int NT, bool HALF, int K, int G>
 __device__ __forceinline__ void merge_part_kg(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
-                                     int part, int n_parts, const DCP_LDS float* w, void* out,
+                                     int e0, int e1, const DCP_LDS float* w, void* out,
                                      int out_bf16) {
   const int tid = threadIdx.x;
-  const int T = 128 * nh;
-  const int e0 = (int)((long long)part * T / n_parts), e1 = (int)((long long)(part + 1) * T / n_parts);
   const WsPartials<HALF> ws(p, part0, n_in);
   const unsigned part_bytes = ws.part_bytes;
   const unsigned blk_off = (unsigned)h0 * 128u * ws.kElem;
@@ -199,20 +204,19 @@ __device__ __forceinline__ void merge_part_kg(const DecodeParams& p, long long p
 // registers do not add to the calling kernel's.
 template <int NT, bool HALF>
 __device__ __attribute__((noinline)) void merge_part_many(const DecodeParams& p, long long part0,
-                                                          int n_in, int h0, int nh, int part,
-                                                          int n_parts, const DCP_LDS float* w,
-                                                          void* out, int out_bf16) {
-  if (n_in <= 16) merge_part_kg<NT, HALF, 2, 16>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
-  else merge_part_kg<NT, HALF, 1, 32>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
+                                                          int n_in, int h0, int nh, int e0, int e1,
+                                                          const DCP_LDS float* w, void* out,
+                                                          int out_bf16) {
+  if (n_in <= 16) merge_part_kg<NT, HALF, 2, 16>(p, part0, n_in, h0, nh, e0, e1, w, out, out_bf16);
+  else merge_part_kg<NT, HALF, 1, 32>(p, part0, n_in, h0, nh, e0, e1, w, out, out_bf16);
 }
 
 // Up to 4 members: 8 elements per thread, the members' loads together.
 template <int NT, bool HALF>
 __device__ __forceinline__ void merge_part(const DecodeParams& p, long long part0, int n_in, int h0, int nh,
-                                  int part, int n_parts, const DCP_LDS float* w, void* out,
-                                  int out_bf16) {
-  if (n_in <= 4) merge_part_kg<NT, HALF, 8, 4>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
-  else merge_part_many<NT, HALF>(p, part0, n_in, h0, nh, part, n_parts, w, out, out_bf16);
+                                  int e0, int e1, const DCP_LDS float* w, void* out, int out_bf16) {
+  if (n_in <= 4) merge_part_kg<NT, HALF, 8, 4>(p, part0, n_in, h0, nh, e0, e1, w, out, out_bf16);
+  else merge_part_many<NT, HALF>(p, part0, n_in, h0, nh, e0, e1, w, out, out_bf16);
 }
 
 // Merges this block's own part (member `member` of NIN = 4 or 8: dim tiles
@@ -448,8 +452,9 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
       const long long part0 = (row * N + shard) * S;
       merge_weights<NT>(p, part0, S, h0, nh, p.lse_part + ((long long)shard * p.rows + row) * H, true, w,
                         nullptr);
-      merge_part<NT, false>(p, part0, S, h0, nh, 0, 1, w,
-                     p.o_part + ((long long)shard * p.rows + row) * H * kVDim, 0);
+      const int2 er = part_range(0, 1, 1, nh);
+      merge_part<NT, false>(p, part0, S, h0, nh, er.x, er.y, w,
+                            p.o_part + ((long long)shard * p.rows + row) * H * kVDim, 0);
       if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
@@ -537,12 +542,21 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   } else {
     merge_weights<NT>(p, part0, n_in, h0, nh, out_lse, last, w, half_ws ? wx : nullptr);
   }
-  for (int m = 0; m < n_in; ++m) {
-    if (own && m == member) continue;
-    if (!(all || m == member || (m < kMaxWaitMembers && ((abandoned >> m) & 1ull)))) continue;
-    if (half_ws) merge_part<NT, true>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
-    else merge_part<NT, false>(p, part0, n_in, h0, nh, m, n_in, w, out, p.out_bf16);
-    ++merged;
+  // Runs of consecutive parts go through the merge as one element range, so
+  // that a block merging many parts keeps all its threads' loads in flight.
+  auto want = [&](int m) {
+    return !(own && m == member) &&
+           (all || m == member || (m < kMaxWaitMembers && ((abandoned >> m) & 1ull)));
+  };
+  for (int m = 0; m < n_in;) {
+    if (!want(m)) { ++m; continue; }
+    int m1 = m + 1;
+    while (m1 < n_in && want(m1)) ++m1;
+    const int2 er = part_range(m, m1, n_in, nh);
+    if (half_ws) merge_part<NT, true>(p, part0, n_in, h0, nh, er.x, er.y, w, out, p.out_bf16);
+    else merge_part<NT, false>(p, part0, n_in, h0, nh, er.x, er.y, w, out, p.out_bf16);
+    merged += m1 - m;
+    m = m1;
   }
   __syncthreads();
   if (tid == 0) {
