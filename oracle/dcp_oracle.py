@@ -115,14 +115,12 @@ def dequant_rows(pool, rows, kv_dtype, scale=None):
 # Step 1: index remap ([P3] Modifications, Index remap)
 # ---------------------------------------------------------------------------
 
-def remap_topk(table, num_shards, pool_rows=None, ascending=False):
+def remap_topk(table, num_shards, pool_rows=None):
     """Global top-k slot table -> per-shard compacted local slot ids and counts.
 
     For shard r and row i: keep the entries g >= 0 of row i with g mod N == r,
     in their original order, replace each by g div N, put them at the front of
     the row and record how many there are.  The rest of the row is -1.
-    ``ascending``: the kept local ids in increasing order instead (the same
-    set; attention over a row does not depend on the order of its tokens).
 
     Returns (local [N, R, k] int32, counts [N, R] int32).
     Preconditions (asserted): the valid entries of a row are distinct and, when
@@ -141,8 +139,6 @@ def remap_topk(table, num_shards, pool_rows=None, ascending=False):
             assert (valid < n * int(pool_rows)).all(), "slot beyond the pool"
         for r in range(n):
             own = valid[valid % n == r] // n
-            if ascending:
-                own = np.sort(own)
             local[r, i, : own.size] = own
             counts[r, i] = own.size
     return local, counts

@@ -71,24 +71,6 @@ def test_remap_hand_worked_fixture():
     local, counts = oracle.remap_topk(np.array(d["table"]), d["num_shards"])
     np.testing.assert_array_equal(local, np.array(d["local"]))
     np.testing.assert_array_equal(counts, np.array(d["counts"]))
-    local, counts = oracle.remap_topk(np.array(d["table"]), d["num_shards"], ascending=True)
-    np.testing.assert_array_equal(local, np.array(d["local_ascending"]))
-    np.testing.assert_array_equal(counts, np.array(d["counts"]))
-
-
-def test_remap_ascending_is_the_sorted_stable_remap():
-    # same counts, each row's kept ids the stable remap's, in Python's sorted order
-    p = wl.preset("sparse_bf16_b8_k2048")
-    rng = np.random.default_rng(6)
-    table = wl.make_topk_table(p, wl.make_block_table(p, rng), rng)
-    stable, c1 = oracle.remap_topk(table, p.num_shards)
-    asc, c2 = oracle.remap_topk(table, p.num_shards, ascending=True)
-    np.testing.assert_array_equal(c1, c2)
-    for r in range(p.num_shards):
-        for i in range(p.rows):
-            c = int(c1[r, i])
-            assert list(asc[r, i, :c]) == sorted(int(x) for x in stable[r, i, :c])
-            assert (asc[r, i, c:] == -1).all()
 
 
 def _check_remap_invariants(table, n, local, counts):

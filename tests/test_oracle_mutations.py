@@ -65,8 +65,6 @@ MUTATIONS = [
      "pos = np.arange(int(n_local), dtype=np.int64) + int(shard) * int(n_local)"),
     ("merge keeps the first shard only", "sc = np.concatenate([np.asarray(c, dtype=np.float64) for c in cand_scores])",
      "sc = np.concatenate([np.asarray(c, dtype=np.float64) for c in cand_scores[:1]] + [np.full(len(c), -np.inf) for c in cand_scores[1:]])"),
-    ("ascending remap left unsorted", "                own = np.sort(own)", "                own = own"),
-    ("ascending remap descending", "                own = np.sort(own)", "                own = np.sort(own)[::-1]"),
     ("kv write keeps skipped", "        if g < 0:\n            continue\n        r, row",
      "        if g < -1:\n            continue\n        r, row"),
 ]
