@@ -148,8 +148,9 @@ dcp_status dcp_remap_topk(const int32_t* topk_global, int64_t rows, int32_t k,
  * (0 = library default); want_partials / want_merged = whether
  * (o_part, lse_part) / (o, lse) will be given.  Returns 0 when the call needs
  * no workspace, and SIZE_MAX for arguments the decode call would reject.
- * The first bytes hold arrival and completion counters: zero the workspace
- * once after allocating it; every call leaves the counters zeroed again.
+ * The first bytes hold the merge's arrival counters: zero the workspace once
+ * after allocating it; every call leaves them ready for the next call (counts
+ * and flags cleared, a generation byte advanced).
  * Calls that share one workspace must be ordered on one stream.
  *
  * Merge scheduling.  When the whole grid of a call fits on the device at
@@ -220,7 +221,7 @@ dcp_status mla_sparse_decode_lse(const void* q, int64_t rows, int32_t heads,
  *     rows too much) returns DCP_ERR_SCRATCH_TOO_SMALL before queuing anything.
  *   - Every call on one GPU shares that GPU's scratch, which keeps the last
  *     call's partials.  The counters start at zero and every call leaves them
- *     zero; calls that overlap on one GPU (other streams, other threads, an
+ *     ready for the next (counts and flags cleared); calls that overlap on one GPU (other streams, other threads, an
  *     unordered graph) race and give wrong results: order them.
  *   - The first call on a device looks up the scratch's device address and
  *     queues a small kernel on `stream` that clears the counters.
@@ -380,7 +381,8 @@ dcp_status dcp_gather_prefix(const int32_t* block_table, int32_t max_pages, int3
                              int32_t max_len, void* out_kv, float* out_scale, hipStream_t stream);
 
 /* Workspace bytes of mla_prefill_chunk_lse (0 = none; SIZE_MAX for arguments
- * it would reject).  Zero it once after allocating; calls leave it zeroed. */
+ * it would reject).  Zero it once after allocating; calls leave it ready for
+ * the next call. */
 size_t dcp_prefill_workspace_size(int64_t tokens, int32_t heads, int64_t chunk_len);
 
 /*

@@ -194,7 +194,7 @@ def workspace_size(dense, rows, heads, num_shards, tokens_per_shard, page_size=6
 
 
 def alloc_workspace(nbytes, device):
-    """Zeroed once; the library leaves its counters zeroed after every call."""
+    """Zeroed once; every call leaves the library's counters ready for the next."""
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 

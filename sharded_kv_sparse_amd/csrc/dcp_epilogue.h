@@ -28,8 +28,10 @@
 // (large grids, many partials, or a zero time limit) every block arrives
 // with its part marked abandoned, and the last arriver merges everything.
 // Partials are added in index order, so the result does not depend on
-// which block merges.  The block that completes the last part resets the
-// arrival and completion words, so the workspace needs zeroing only once.
+// which block merges.  The last arriver starts the arrival word's next
+// generation (count and abandon bits cleared) as soon as it has read it, and
+// the blocks that wait watch for that generation change: the workspace needs
+// zeroing only once, and no block waits for the others to finish merging.
 #pragma once
 
 #include <type_traits>
@@ -39,7 +41,7 @@
 
 namespace dcp {
 
-constexpr int kMaxWaitMembers = 56;         // abandon bits 8..63 of the 64-bit arrival word
+constexpr int kMaxWaitMembers = 48;         // abandon bits 8..55 of the 64-bit arrival word
 
 // Weights of the n_in partials of a head block, from their LSEs: w[i][hl]
 // (normalised), and the merged LSE of each head written to out_lse when
@@ -462,15 +464,21 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   if (!fused) return;
 
   // ---- all partials of the row -> o.  Arrival word (64 bits): count in
-  // bits 0..7, abandoned parts in bits 8 + member.  Completion word: parts
-  // merged.  Four 32-bit counter words per (row, head block).
+  // bits 0..7, abandoned parts in bits 8 + member, generation in bits
+  // 56..63.  Four 32-bit counter words per (row, head block), the first two
+  // used.  Every member has arrived once the generation differs from the
+  // one its own arrival saw (or, before the last arriver has moved it on,
+  // the count has reached n_in).
   unsigned long long* arrive = reinterpret_cast<unsigned long long*>(p.cnt_row + (row * HB + hblk) * 4);
-  unsigned* done = reinterpret_cast<unsigned*>(p.cnt_row + (row * HB + hblk) * 4 + 2);
+  unsigned long long gen0 = 0;           // (thread 0) generation at this block's arrival
+  auto all_in = [&](unsigned long long now) {
+    return (now >> 56) != gen0 || (now & 0xffull) == (unsigned long long)n_in;
+  };
   // Abandons this block's part: with an own part kept in registers, that
   // part is stored (and waited for) first.  Returns the parts to merge.
   auto give_up = [&](unsigned long long now) -> unsigned {
     for (;;) {
-      if ((now & 0xffull) == (unsigned long long)n_in) return 1u;
+      if (all_in(now)) return 1u;
       unsigned long long expect = now;
       if (__hip_atomic_compare_exchange_strong(arrive, &expect, now | (1ull << (8 + member)),
                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -484,16 +492,20 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
         1ull + (!may_wait && n_in <= kMaxWaitMembers ? 1ull << (8 + member) : 0ull);
     const unsigned long long old =
         __hip_atomic_fetch_add(arrive, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    gen0 = old >> 56;
     unsigned parts = 0u;                 // bit 0: own part; bit 1: last arriver
     if ((old & 0xffull) == (unsigned long long)n_in - 1) {
       parts = 3u;
       *s_seen = old;
+      // every member is in and the abandon bits are read: next generation
+      __hip_atomic_store(arrive, ((gen0 + 1ull) & 0xffull) << 56, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     } else if (may_wait) {
       const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
       for (;;) {
         const unsigned long long now =
             __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((now & 0xffull) == (unsigned long long)n_in) { parts = 1u; break; }
+        if (all_in(now)) { parts = 1u; break; }
         if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)p.merge_wait_ticks) {
           if (own) {
             parts = 4u;                  // timed out: store the own part first
@@ -527,18 +539,16 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   // The last arriver merges every part whose member gave up (all parts
   // when there are too many members for abandon bits).
   const bool all = (parts & 2u) && n_in > kMaxWaitMembers;
-  const unsigned long long abandoned = (parts & 2u) ? (*s_seen >> 8) : 0ull;
+  const unsigned long long abandoned = (parts & 2u) ? (*s_seen >> 8) & ((1ull << kMaxWaitMembers) - 1) : 0ull;
 
   void* out = p.out_bf16 ? (void*)(static_cast<unsigned short*>(p.o) + row * H * kVDim)
                          : (void*)(static_cast<float*>(p.o) + row * H * kVDim);
   const long long part0 = row * N * S;
-  int merged = 0;
   float* out_lse = p.lse + row * H;
   const bool last = (parts & 2u) != 0u;
   if (own && (parts & 1u)) {       // (own implies the fp16 workspace)
     merge_own_part<NT, 4, true>(p, part0, member, h0, nh, hl, g, own_v, w, wx, out_lse, last, out,
                                 p.out_bf16);
-    ++merged;
   } else {
     merge_weights<NT>(p, part0, n_in, h0, nh, out_lse, last, w, half_ws ? wx : nullptr);
   }
@@ -555,17 +565,7 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
     const int2 er = part_range(m, m1, n_in, nh);
     if (half_ws) merge_part<NT, true>(p, part0, n_in, h0, nh, er.x, er.y, w, out, p.out_bf16);
     else merge_part<NT, false>(p, part0, n_in, h0, nh, er.x, er.y, w, out, p.out_bf16);
-    merged += m1 - m;
     m = m1;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(done, (unsigned)merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev + (unsigned)merged == (unsigned)n_in) {
-      __hip_atomic_store(arrive, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 

@@ -8,11 +8,11 @@
 // device address is looked up once with hipGetSymbolAddress and kept per
 // device; kernels receive that address.
 //
-// Layout: the first DCP_NOALLOC_COUNTER_BYTES hold the merge's arrival and
-// completion counters, which must be zero when a call starts.  They are
-// zero when the code object is loaded, are cleared once more by a fill
+// Layout: the first DCP_NOALLOC_COUNTER_BYTES hold the merge's arrival
+// counters, whose counts and flags must be clear when a call starts.  They
+// are zero when the code object is loaded, are cleared once more by a fill
 // kernel queued at the first call on each device, and every decode call
-// leaves them zero again.  The rest holds the per-block partials of the
+// leaves its counts and flags clear again (a generation byte advances).  The rest holds the per-block partials of the
 // fused merge, which each call writes before it reads them.
 #include <mutex>
 

@@ -288,7 +288,11 @@ def test_fused_equals_unfused_and_counters_reset(gpu):
     torch.cuda.synchronize()
     assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
     hb = (p.heads + 63) // 64
-    assert (ws[: 8 * p.rows * hb].view(torch.int32) == 0).all()    # arrival + completion words
+    # arrival words (64 bits, the first of two per (row, head block)): count
+    # and abandon bits clear after every call, the generation byte moved on
+    words = ws[: 16 * p.rows * hb].view(torch.int64).view(p.rows * hb, 2)[:, 0].cpu().numpy()
+    assert ((words.astype(np.uint64) & np.uint64((1 << 56) - 1)) == 0).all()
+    assert (words.astype(np.uint64) >> np.uint64(56) == 2).all()      # two fused calls
     # The fused merge exchanges the partials as fp16 with a power of two per
     # (partial, head) that puts the head's largest magnitude in [2^14, 2^15):
     # every value is off by at most 2^-11 of its head's largest partial value
@@ -303,7 +307,8 @@ def test_fused_equals_unfused_and_counters_reset(gpu):
 def test_fused_merge_modes_agree(gpu, name):
     # The row's blocks share the merge (bounded wait), give up at once (1 us),
     # or never wait (the last block merges everything): bit-identical results,
-    # counters back at zero every time, and within tolerance of the oracle.
+    # arrival counts and flags clear after every call (the generation byte
+    # advancing by one per call), and within tolerance of the oracle.
     p = wl.preset(name)
     w = make(p)
     table = w.dev(w.table)
@@ -313,7 +318,7 @@ def test_fused_merge_modes_agree(gpu, name):
     ws = B.alloc_workspace(nb, gpu)
     hb = (p.heads + 63) // 64
     res = {}
-    for us in ["30", "1", "0", "30"]:
+    for call, us in enumerate(["30", "1", "0", "30"]):
         say(f"merge wait {us} us")
         B.set_merge_wait_us(int(us))
         try:
@@ -321,7 +326,9 @@ def test_fused_merge_modes_agree(gpu, name):
             torch.cuda.synchronize()
         finally:
             B.set_merge_wait_us(30)
-        assert (ws[: 8 * p.rows * hb].view(torch.int32) == 0).all()
+        words = ws[: 16 * p.rows * hb].view(torch.int64).view(p.rows * hb, 2)[:, 0].cpu().numpy()
+        assert ((words.astype(np.uint64) & np.uint64((1 << 56) - 1)) == 0).all()
+        assert (words.astype(np.uint64) >> np.uint64(56) == call + 1).all()
         if us in res:
             assert torch.equal(r["o"], res[us]["o"]) and torch.equal(r["lse"], res[us]["lse"])
         res[us] = r
