@@ -136,6 +136,35 @@ def flops(p, tokens):
     return 2.0 * p.heads * tokens * (576 + 512)
 
 
+def fp8_kernel_mfma(p, w, splits):
+    """MFMAs the FP8 decode kernel (64 or 128 heads) executes for one launch.
+
+    Per wave (16 heads) and 128-token tile: 8 S tiles x (4 latent k-steps x 2
+    query terms + 1 RoPE k-step) + 32 dim tiles x 3 P' terms = 168; a tile of
+    at most 64 valid tokens (the remainder past whole tiles) skips half the
+    S tiles and packs its P' terms into two MFMAs per dim tile: 100.  Every
+    MFMA is 16x16x128, 65,536 flops.  None for the other kernels."""
+    if p.kv_dtype != "fp8" or p.heads not in (64, 128):
+        return None
+    n_sh = p.num_shards
+    if p.kind == "sparse":
+        counts = np.zeros((n_sh, p.rows), dtype=np.int64)
+        for r in range(n_sh):
+            counts[r] = ((w.table >= 0) & (w.table % n_sh == r)).sum(axis=1)
+    else:
+        cap = p.lpages * p.page_size
+        counts = np.minimum(np.repeat(w.local_lens, p.q_per_seq, axis=1), cap).astype(np.int64)
+    per_wave = 0
+    for n in counts.ravel():
+        chunk = -(-(-(-int(n) // splits)) // 128) * 128
+        for sp in range(splits):
+            ln = max(0, min(int(n), (sp + 1) * chunk) - min(int(n), sp * chunk))
+            tiles, rem = -(-ln // 128), ln % 128
+            short = 1 if 0 < rem <= 64 else 0
+            per_wave += 168 * (tiles - short) + 100 * short
+    return per_wave * 4 * (p.heads // 64)
+
+
 def measure_kv_write(w, stream, dev, reps=50):
     """Time dcp_kv_write on layer 0 of group w: the new tokens of one decode
     step (q_per_seq per sequence) and a chunk of up to 2048 tokens per sequence, both
@@ -173,6 +202,36 @@ def measure_kv_write(w, stream, dev, reps=50):
                       "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     return out
+
+
+def measure_combine(p, stream, dev, reps=50):
+    """The standalone LSE merge (lse_combine) of per-shard partials of the
+    decode workload's shape: fp32 [N, rows, heads, 512] + LSE in, bf16 out,
+    one shard's LSE -inf on every fourth row.  Events around `reps` launches
+    on the launch stream."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    n, rows, heads = p.num_shards, p.rows, p.heads
+    o_part = torch.randn((n, rows, heads, 512), generator=gen, device=dev)
+    lse_part = torch.randn((n, rows, heads), generator=gen, device=dev) * 3
+    lse_part[0, ::4] = float("-inf")
+    o = torch.empty((rows, heads, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((rows, heads), dtype=torch.float32, device=dev)
+    call = lambda: B.lse_combine(o_part, lse_part, B.OUT_BF16, o, lse, stream=stream)  # noqa: E731
+    for _ in range(5):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    alg = n * rows * heads * (512 + 1) * 4 + rows * heads * (512 * 2 + 4)
+    return {"workload": f"{p.name} partials ({n} shards)", "us_per_launch": round(us, 2),
+            "algorithmic_bytes": alg, "gbps": round(alg / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def measure_prefill(stream, dev, reps=20, name="prefill_fp8_prefix16k_new2k"):
@@ -546,6 +605,22 @@ def main():
         achieved = tot_b / (dec_mean * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    # The FP8 kernel's executed MFMA work (query hi + lo terms, three P'
+    # terms, padded short tiles) against the fp8 MFMA peak, beside the roof
+    # above: which of the two binds depends on the shape.
+    splits = B.decode_splits(not sparse, p.rows, p.heads, p.num_shards,
+                             p.topk if sparse else int(groups[0].local_lens.max()), p.page_size,
+                             args.num_splits)
+    mfma_n = [fp8_kernel_mfma(p, w, splits) for w in groups]
+    if mfma_n[0] is not None:
+        ex_flops = statistics.mean(mfma_n) * 65536.0
+        ex_tf = ex_flops / (dec_mean * 1e-6) / 1e12
+        roof["mfma_executed"] = {"mfma_per_launch": int(statistics.mean(mfma_n)),
+                                 "flops_per_launch": ex_flops, "achieved": round(ex_tf, 1),
+                                 "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(ex_tf / FP8_MFMA_PEAK_TFLOPS, 4),
+                                 "floor_us": round(ex_flops / (FP8_MFMA_PEAK_TFLOPS * 1e12) * 1e6, 2)}
+    roof["splits"] = splits
     roof.update({"kernel": kname + (" (fused sparse MLA decode + LSE merge)" if sparse
                                     else " (fused dense MLA decode + LSE merge)"),
                  "avg_launch_us": round(dec_mean, 2), "algorithmic_bytes_per_launch": int(tot_b),
@@ -600,12 +675,8 @@ def main():
     # The KV-cache write runs after the timed decode loop (it overwrites the
     # last positions of layer 0 of the first table group).
     result["kv_write"] = measure_kv_write(groups[0], stream, dev)
-    if not args.no_prefill:
-        del groups, prep
-        torch.cuda.empty_cache()
-        result["prefill_prefix"] = measure_prefill(stream, dev)
-        torch.cuda.empty_cache()
-        result["index_topk"] = measure_topk(stream, dev)
+    # The oracle's baseline runs on a host copy of layer 0 of the first table
+    # group, before the layer caches are released for the other measurements.
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: copying one layer to the host", file=sys.stderr, flush=True)
         w = groups[0]
@@ -615,6 +686,14 @@ def main():
         print("[bench] cpu baseline: running the oracle", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, host, args.cpu_rows)
         result["cpu_baseline"] = cb
+        del w, host
+    if not args.no_prefill:
+        del groups, prep
+        torch.cuda.empty_cache()
+        result["combine"] = measure_combine(p, stream, dev)
+        result["prefill_prefix"] = measure_prefill(stream, dev)
+        torch.cuda.empty_cache()
+        result["index_topk"] = measure_topk(stream, dev)
     line = json.dumps(result)
     print(line, flush=True)
     if args.out:

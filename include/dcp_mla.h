@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DCP_ABI_VERSION 3
+#define DCP_ABI_VERSION 4
 #define DCP_HEAD_DIM 576
 #define DCP_V_DIM 512
 #define DCP_MAX_SHARDS 16
@@ -165,6 +165,19 @@ size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
                                  int32_t num_shards, int64_t tokens_per_shard,
                                  int32_t page_size, int32_t num_splits,
                                  int32_t want_partials, int32_t want_merged);
+
+/*
+ * The token splits per (row, shard) that a decode call with these arguments
+ * uses (same arguments as dcp_decode_workspace_size, without the outputs):
+ * num_splits itself when it is > 0 and allowed, else the library's default
+ * for the shape.  Returns -1 for arguments the decode call would reject.
+ * Split s of a row's n local tokens covers [s * c, min(n, (s + 1) * c)) with
+ * c = ceil(ceil(n / splits) / T) * T, T the kernel's tile: 128 tokens for FP8
+ * KV with 64 or 128 heads, 64 otherwise.  Informational: a caller never
+ * needs it to run a decode.
+ */
+int32_t dcp_decode_splits(int32_t dense, int64_t rows, int32_t heads, int32_t num_shards,
+                          int64_t tokens_per_shard, int32_t page_size, int32_t num_splits);
 
 /*
  * Step 2 (+ step 3 fused) -- sparse absorbed-MLA decode with LSE over the

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdcpmla.so")
 
-ABI_VERSION = 3           # DCP_ABI_VERSION this binding's structures follow
+ABI_VERSION = 4           # DCP_ABI_VERSION this binding's structures follow
 HEAD_DIM = 576
 V_DIM = 512
 MAX_SHARDS = 16
@@ -27,7 +27,7 @@ KV_BF16, KV_FP8_E4M3 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 
 EXPORTS = ("dcp_status_string", "dcp_abi_version", "dcp_set_merge_wait_us", "dcp_remap_topk",
-           "dcp_decode_workspace_size", "mla_sparse_decode_lse", "mla_sparse_decode_lse_noalloc",
+           "dcp_decode_workspace_size", "dcp_decode_splits", "mla_sparse_decode_lse", "mla_sparse_decode_lse_noalloc",
            "mla_dense_decode_lse",
            "lse_combine", "dcp_kv_write", "dcp_gather_prefix", "dcp_prefill_workspace_size",
            "mla_prefill_chunk_lse", "lse_merge_into", "dcp_index_score", "dcp_topk_local",
@@ -75,6 +75,8 @@ def lib():
     L.dcp_remap_topk.restype = ctypes.c_int
     L.dcp_decode_workspace_size.argtypes = [i32, i64, i32, i32, i64, i32, i32, i32, i32]
     L.dcp_decode_workspace_size.restype = sz
+    L.dcp_decode_splits.argtypes = [i32, i64, i32, i32, i64, i32, i32]
+    L.dcp_decode_splits.restype = i32
     L.mla_sparse_decode_lse.argtypes = [vp, i64, i32, ctypes.POINTER(KvShard), i32, ctypes.c_int,
                                         vp, vp, i32, f32, vp, vp, vp, vp, ctypes.c_int, i32,
                                         vp, sz, vp]
@@ -191,6 +193,15 @@ def workspace_size(dense, rows, heads, num_shards, tokens_per_shard, page_size=6
     if n == ctypes.c_size_t(-1).value:
         raise DcpError(1, "dcp_decode_workspace_size")
     return n
+
+
+def decode_splits(dense, rows, heads, num_shards, tokens_per_shard, page_size=64, num_splits=0):
+    """Token splits per (row, shard) a decode call with these arguments uses."""
+    s = lib().dcp_decode_splits(int(bool(dense)), rows, heads, num_shards, tokens_per_shard,
+                                page_size, num_splits)
+    if s < 0:
+        raise DcpError(1, "dcp_decode_splits")
+    return s
 
 
 def alloc_workspace(nbytes, device):

@@ -385,6 +385,18 @@ size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
   return plan_workspace(rows, heads, num_shards, splits, want_partials != 0, want_merged != 0).total;
 }
 
+int32_t dcp_decode_splits(int32_t dense, int64_t rows, int32_t heads, int32_t num_shards,
+                          int64_t tokens_per_shard, int32_t page_size, int32_t num_splits) {
+  if (rows < 0 || heads < 1 || num_shards < 1 || num_shards > kMaxShards || tokens_per_shard < 0)
+    return -1;
+  if (dense && page_size < 1) return -1;
+  int splits = 0;
+  if (plan_splits(dense != 0, std::max<int64_t>(rows, 1), num_shards, heads, tokens_per_shard, page_size,
+                  num_splits, &splits) != DCP_OK)
+    return -1;
+  return splits;
+}
+
 dcp_status mla_sparse_decode_lse(const void* q, int64_t rows, int32_t heads,
                                  const dcp_kv_shard* shards, int32_t num_shards,
                                  dcp_kv_dtype kv_dtype, const int32_t* topk_local,

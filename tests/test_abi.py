@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.dcp_abi_version() == B.ABI_VERSION == 3
+    assert L.dcp_abi_version() == B.ABI_VERSION == 4
     for code, name in B.STATUS_NAMES.items():
         assert L.dcp_status_string(code).decode() == name
     assert L.dcp_status_string(99).decode() == "DCP_ERR_UNKNOWN"
@@ -277,6 +277,23 @@ def test_workspace_size_rules(L):
     assert ws(0, 64, 64, 4, 2048, 1, 2, 0, 1) > fused                  # more splits, more partials
     assert ws(0, 128, 64, 4, 2048, 1, 1, 0, 1) > fused
     assert ws(0, 64, 64, 4, 2048, 1, 2, 1, 1) >= ws(0, 64, 64, 4, 2048, 1, 2, 0, 1)
+
+
+def test_decode_splits_rules(L):
+    sp = lambda *a: L.dcp_decode_splits(*a)                            # noqa: E731
+    # (dense, rows, heads, shards, tokens, page, splits)
+    assert sp(0, 64, 64, 0, 2048, 1, 0) == -1
+    assert sp(0, -1, 64, 4, 2048, 1, 0) == -1
+    assert sp(1, 4, 64, 2, 64, 0, 0) == -1                           # dense needs a page size
+    assert sp(0, 64, 64, 4, 2048, 1, 0) == 1                          # 256 (row, shard) units fill the chip
+    assert sp(0, 8, 64, 4, 2048, 1, 0) == 4                           # 32 units: 4 splits of 128 tokens
+    assert sp(0, 8, 64, 4, 2048, 1, 8) == 8                           # asked for
+    assert sp(0, 8, 64, 4, 2048, 1, 17) == -1                         # 17 x 4 partials: too many to merge
+    # the workspace query plans the same splits
+    for args in [(0, 8, 64, 4, 2048, 1), (1, 32, 128, 8, 131072, 64), (0, 96, 32, 2, 2048, 1)]:
+        s = sp(*args, 0)
+        assert s >= 1
+        assert L.dcp_decode_workspace_size(*args, s, 0, 1) == L.dcp_decode_workspace_size(*args, 0, 0, 1)
 
 
 def test_binding_refuses_without_gpu_tensors():

@@ -6,6 +6,7 @@ scale per selected token, 2 x (576 + 512) flops per token and head)."""
 import types
 
 import bench
+import numpy as np
 from sharded_kv_sparse_amd import workloads as wl
 
 
@@ -28,3 +29,21 @@ def test_bf16_workload_bytes_per_token():
     p = wl.preset("sparse_bf16_b8_k2048")
     kv, _ = bench.algorithmic_bytes(types.SimpleNamespace(p=p), 1000)
     assert kv == 1000 * 1152
+
+
+def test_fp8_kernel_mfma_hand_worked():
+    # one shard, 64 heads: row 0 holds 200 tokens (a full tile and one of 72
+    # tokens: 2 x 168 MFMAs per wave), row 1 holds 64 (one short tile: 100);
+    # four waves per block.  Two splits cut row 0 into 128 + 72 and row 1
+    # into 64 + 0: the same tiles.
+    from types import SimpleNamespace
+    p = SimpleNamespace(kv_dtype="fp8", heads=64, kind="sparse", num_shards=1, rows=2)
+    table = np.full((2, 256), -1, dtype=np.int64)
+    table[0, :200] = np.arange(200)
+    table[1, :64] = np.arange(64)
+    w = SimpleNamespace(table=table)
+    assert bench.fp8_kernel_mfma(p, w, 1) == 4 * (2 * 168 + 100) == 1744
+    assert bench.fp8_kernel_mfma(p, w, 2) == 1744
+    p128 = SimpleNamespace(**{**vars(p), "heads": 128})
+    assert bench.fp8_kernel_mfma(p128, w, 1) == 2 * 1744            # two 64-head blocks
+    assert bench.fp8_kernel_mfma(SimpleNamespace(**{**vars(p), "kv_dtype": "bf16"}), w, 1) is None
