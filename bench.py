@@ -376,9 +376,10 @@ def measure_topk(stream, dev, reps=20, name="index_topk_b64_ctx128k_k2048"):
                   "frac_hbm_peak": round(s_bytes / (per[0] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                   "tflops": round(s_flops / (per[0] * 1e-6) / 1e12, 1),
                   "algorithmic_bytes": int(s_bytes)},
-        "local_topk": {"kernel": "topk_select_kernel (local)", "us": round(per[1], 2),
+        "local_topk": {"kernel": "topk_local_fast_kernel (lists of at most 32,768 tokens)",
+                       "us": round(per[1], 2),
                        "lists": p.rows * p.num_shards, "list_len": p.max_local},
-        "merge": {"kernel": "topk_select_kernel (merge)", "us": round(per[2], 2),
+        "merge": {"kernel": "topk_merge_rank_kernel", "us": round(per[2], 2),
                   "candidates_per_row": p.num_shards * p.topk},
     }
 
