@@ -492,7 +492,10 @@ void decode_fp8_kernel(const DecodeParams p) {
     }
 
     // First V^T operands, read before the softmax so their latency hides.
-    constexpr int NR = 4;                          // tr8 reads per dim tile
+    // The short lead tile's 64 tokens need only the first two tr8 reads of a
+    // dim tile, and its softmax only the first four S tiles.
+    constexpr int NR = first_short ? 2 : 4;        // tr8 reads per dim tile
+    constexpr int NSS = first_short ? 4 : NS;      // S tiles the softmax covers
     i32x2 vr[2][2][NR];
     auto load_v = [&](int d, i32x2* r4) {
 #pragma unroll
@@ -511,7 +514,7 @@ void decode_fp8_kernel(const DecodeParams p) {
     float tmax = kNegInf;
     const bool full = tok0 + kT <= tend;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
+    for (int st = 0; st < NSS; ++st) {
       const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[st][i] = sacc[st][i] * s4[i];
@@ -519,13 +522,13 @@ void decode_fp8_kernel(const DecodeParams p) {
     copy_at(9);
     if (!full) {                           // the last tile of the row: mask its tail
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+      for (int st = 0; st < NSS; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (tok0 + 16 * st + 4 * g + i >= tend) z[st][i] = kNegInf;
     }
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
+    for (int st = 0; st < NSS; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[st][i]);
     tmax = max_xor32(max_xor16(tmax));
@@ -545,7 +548,7 @@ void decode_fp8_kernel(const DecodeParams p) {
     float (&pr)[NS][4] = z;                // P' = p * scale replaces the logits
     float pmax = 0.f;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
+    for (int st = 0; st < NSS; ++st) {
       const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -568,9 +571,9 @@ void decode_fp8_kernel(const DecodeParams p) {
     const int ep = e4m3_exponent(pmax);
     const float ps = pow2i(ep);
     const int pscale = 127 - ep;
-    i32x8 pb[3];                           // pb[term] byte 4st + i
+    i32x8 pb[3] = {};                      // pb[term] byte 4st + i
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
+    for (int st = 0; st < NSS; ++st) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = pr[st][i] * ps;
@@ -586,7 +589,7 @@ void decode_fp8_kernel(const DecodeParams p) {
       pb[1][st] = m;
       pb[2][st] = l;
       if (st == 2) copy_at(12);
-      if (st == 5) copy_at(13);
+      if (st == (NSS > 5 ? 5 : NSS - 1)) copy_at(13);
     }
 
     // ---- The last tile stores the workspace partial during its PV, each
@@ -631,8 +634,10 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const i32x2* r4 = vr[grp & 1][j];
-          vt[j] = sh ? i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[0].x, r4[0].y, r4[1].x, r4[1].y}
-                     : i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
+          if constexpr (sh)
+            vt[j] = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[0].x, r4[0].y, r4[1].x, r4[1].y};
+          else
+            vt[j] = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[NR - 2].x, r4[NR - 2].y, r4[NR - 1].x, r4[NR - 1].y};
         }
         if constexpr (next) {
           if (grp < 4) issue_copy(rc, it + 1, 14 + grp);
@@ -654,8 +659,12 @@ void decode_fp8_kernel(const DecodeParams p) {
       }
       if constexpr (!next) store_pair(15);
     };
-    if (!short_tile) pv(BoolC<false>{});
-    else pv(BoolC<true>{});
+    if constexpr (first_short) {
+      pv(BoolC<true>{});
+    } else {
+      if (!short_tile) pv(BoolC<false>{});
+      else pv(BoolC<true>{});
+    }
   };
   // Tile 0's copies are waited for at its top like any tile's.
   int it = 0;
