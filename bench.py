@@ -72,7 +72,7 @@ def measured_traffic(kernel, workload):
 
 
 def decode_kernel_name(p):
-    if p.kv_dtype == "fp8" and p.heads in (64, 128):
+    if p.kv_dtype == "fp8" and p.heads >= 48:
         return "decode_fp8_kernel"
     return "decode_kernel"
 METRIC = "µs/layer-step and KV HBM GB/s (% of peak), sparse MLA decode B=64 top-k 2048"
@@ -144,7 +144,7 @@ def fp8_kernel_mfma(p, w, splits):
     at most 64 valid tokens (the remainder past whole tiles) skips half the
     S tiles and packs its P' terms into two MFMAs per dim tile: 100.  Every
     MFMA is 16x16x128, 65,536 flops.  None for the other kernels."""
-    if p.kv_dtype != "fp8" or p.heads not in (64, 128):
+    if p.kv_dtype != "fp8" or p.heads < 48:
         return None
     n_sh = p.num_shards
     if p.kind == "sparse":
@@ -162,7 +162,7 @@ def fp8_kernel_mfma(p, w, splits):
             tiles, rem = -(-ln // 128), ln % 128
             short = 1 if 0 < rem <= 64 else 0
             per_wave += 168 * (tiles - short) + 100 * short
-    return per_wave * 4 * (p.heads // 64)
+    return per_wave * 4 * -(-p.heads // 64)      # idle waves of a partial head block included
 
 
 def measure_kv_write(w, stream, dev, reps=50):

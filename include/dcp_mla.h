@@ -60,7 +60,7 @@ extern "C" {
 typedef enum dcp_status {
   DCP_OK = 0,
   DCP_ERR_INVALID_ARGUMENT = 1,  /* null pointer, non-positive size, bad index   */
-  DCP_ERR_UNSUPPORTED = 2,       /* valid but not implemented (e.g. heads = 48)  */
+  DCP_ERR_UNSUPPORTED = 2,       /* valid but not implemented (e.g. heads = 40)  */
   DCP_ERR_WORKSPACE_TOO_SMALL = 3,
   DCP_ERR_LAUNCH = 4,            /* the HIP runtime rejected a kernel launch     */
   DCP_ERR_SCRATCH_TOO_SMALL = 5  /* a no-allocation call needs more than the
@@ -173,7 +173,7 @@ size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
  * for the shape.  Returns -1 for arguments the decode call would reject.
  * Split s of a row's n local tokens covers [s * c, min(n, (s + 1) * c)) with
  * c = ceil(ceil(n / splits) / T) * T, T the kernel's tile: 128 tokens for FP8
- * KV with 64 or 128 heads, 64 otherwise.  Informational: a caller never
+ * KV with 48 heads or more, 64 otherwise.  Informational: a caller never
  * needs it to run a decode.
  */
 int32_t dcp_decode_splits(int32_t dense, int64_t rows, int32_t heads, int32_t num_shards,
@@ -195,8 +195,9 @@ int32_t dcp_decode_splits(int32_t dense, int64_t rows, int32_t heads, int32_t nu
  *   O = sum_r e^{LSE_r - M} O_r / sum_r e^{LSE_r - M},  LSE = M + ln sum(...),
  *   and O = 0, LSE = -inf when every shard is empty.
  *
- *   q            device bf16 [rows, heads, 576]; heads in {16, 32, 64, 128}
- *                (the gathered heads of a DCP group, [P3] Motivation)
+ *   q            device bf16 [rows, heads, 576]; heads a multiple of 16 from
+ *                16 to 128, else DCP_ERR_UNSUPPORTED (the gathered heads of a
+ *                DCP group, [P3] Motivation)
  *   shards       host array [num_shards] of device pool descriptors
  *   topk_local   device int32 [num_shards, rows, k]   (dcp_remap_topk output)
  *   counts       device int32 [num_shards, rows]
@@ -404,13 +405,14 @@ size_t dcp_prefill_workspace_size(int64_t tokens, int32_t heads, int64_t chunk_l
  * token, so each query row attends every chunk token:
  *   z_j = softmax_scale * q[t][h] . K[j],  O[t][h] = sum_j e^{z_j} V[j] / sum_j e^{z_j},
  *   lse[t][h] = ln sum_j e^{z_j};  chunk_len == 0 gives O = 0, lse = -inf.
- *   q          device bf16 [tokens, heads, 576]; heads in {16, 32, 64, 128}
+ *   q          device bf16 [tokens, heads, 576]; heads a multiple of 16 from 16
+ *              to 128, else DCP_ERR_UNSUPPORTED
  *   chunk_kv   device [chunk_len, 576] E4M3FN codes (value = code * chunk_scale)
  *              or bf16, packed rows, 16-byte aligned (dcp_gather_prefix output);
  *              chunk_kv and chunk_scale may be NULL when chunk_len == 0
  *   o, lse     device fp32 [tokens, heads, 512] and [tokens, heads]
- * Runs the dense decode kernels with (token, head) rows regrouped 64 heads to
- * a row, so that a block reads the chunk once for 64 query rows.
+ * Runs the dense decode kernels with the (token, head) queries regrouped 64
+ * to a row, so that a block reads the chunk once for 64 queries.
  */
 dcp_status mla_prefill_chunk_lse(const void* q, int64_t tokens, int32_t heads,
                                  const void* chunk_kv, const float* chunk_scale,

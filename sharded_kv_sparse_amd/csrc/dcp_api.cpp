@@ -16,7 +16,7 @@ namespace {
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-bool valid_heads(int heads) { return heads == 16 || heads == 32 || heads == 64 || heads == 128; }
+bool valid_heads(int heads) { return heads >= 16 && heads <= 128 && heads % 16 == 0; }
 
 // Smallest split count that keeps every block's slot list within its LDS
 // budget (sparse: slot ids; dense: pages).
@@ -52,7 +52,7 @@ dcp_status plan_splits(bool dense, long long rows, int num_shards, int heads,
 }  // namespace
 
 // Token splits per (row, shard): enough blocks to cover the chip once, at
-// least one tile of tokens per split (128 for 64 or 128 heads, the FP8
+// least one tile of tokens per split (128 from 48 heads on, the FP8
 // kernel's tile; 64 for 16 or 32 heads, whose kernel uses 32- or 64-token
 // tiles), at most 32K tokens per split.  Depends on the heads, not the KV
 // dtype, so the workspace size query plans the same splits as the call.
@@ -248,27 +248,25 @@ dcp_status launch_checked(const DecodeParams& p, bool fp8, bool dense, hipStream
   return launch_decode(p, fp8, dense, stream) == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH;
 }
 
-// A prefill chunk's attention as dense decode launches: all query rows attend
-// the same chunk, so (token, head) rows are regrouped into rows of 64 heads
-// (tokens * heads / 64 of them; 64 heads per block read the chunk once), and
-// the tokens left over when 64 / heads does not divide the token count run as
-// a second launch with their own head count.
+// A prefill chunk's attention as dense decode launches: every query of
+// every token attends the same chunk with no mask, so the tokens * heads
+// (token, head) queries, contiguous in that order in q, o and lse, are
+// regrouped into rows of 64 (64 queries per block read the chunk once); the
+// last tokens * heads mod 64 of them (a multiple of 16) run as a second
+// launch of one row with that many heads.
 struct PrefillLaunch {
   long long rows;      // rows of this launch
   int heads;           // heads per row
-  long long tok_off;   // first token of this launch
+  long long pair_off;  // first (token, head) query of this launch
 };
 
 int prefill_launches(long long tokens, int heads, PrefillLaunch out[2]) {
   int n = 0;
-  if (heads >= 64) {
-    out[n++] = PrefillLaunch{tokens * heads / 64, 64, 0};
-    return n;
-  }
-  const long long per = 64 / heads;               // tokens per 64-head row
-  const long long main_tok = tokens / per * per;
-  if (main_tok > 0) out[n++] = PrefillLaunch{main_tok / per, 64, 0};
-  if (tokens > main_tok) out[n++] = PrefillLaunch{tokens - main_tok, heads, main_tok};
+  const long long pairs = tokens * heads;
+  const long long main_rows = pairs / 64;
+  const int rem = (int)(pairs - main_rows * 64);
+  if (main_rows > 0) out[n++] = PrefillLaunch{main_rows, 64, 0};
+  if (rem > 0) out[n++] = PrefillLaunch{1, rem, main_rows * 64};
   return n;
 }
 
@@ -374,7 +372,7 @@ size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
                                  int32_t page_size, int32_t num_splits,
                                  int32_t want_partials, int32_t want_merged) {
   const size_t bad = std::numeric_limits<size_t>::max();
-  if (rows < 0 || heads < 1 || num_shards < 1 || num_shards > kMaxShards || tokens_per_shard < 0)
+  if (rows < 0 || !valid_heads(heads) || num_shards < 1 || num_shards > kMaxShards || tokens_per_shard < 0)
     return bad;
   if (dense && page_size < 1) return bad;
   if (!want_partials && !want_merged) return bad;
@@ -387,7 +385,7 @@ size_t dcp_decode_workspace_size(int32_t dense, int64_t rows, int32_t heads,
 
 int32_t dcp_decode_splits(int32_t dense, int64_t rows, int32_t heads, int32_t num_shards,
                           int64_t tokens_per_shard, int32_t page_size, int32_t num_splits) {
-  if (rows < 0 || heads < 1 || num_shards < 1 || num_shards > kMaxShards || tokens_per_shard < 0)
+  if (rows < 0 || !valid_heads(heads) || num_shards < 1 || num_shards > kMaxShards || tokens_per_shard < 0)
     return -1;
   if (dense && page_size < 1) return -1;
   int splits = 0;
@@ -486,7 +484,7 @@ dcp_status mla_prefill_chunk_lse(const void* q, int64_t tokens, int32_t heads,
   PrefillLaunch l[2];
   const int n = prefill_launches(tokens, heads, l);
   for (int i = 0; i < n; ++i) {
-    const long long off = l[i].tok_off * heads;           // first (token, head) row
+    const long long off = l[i].pair_off;                   // first (token, head) query
     CommonArgs a{static_cast<const char*>(q) + off * kHeadDim * 2, l[i].rows, l[i].heads, &chunk, 1,
                  kv_dtype, softmax_scale, o + off * kVDim, lse + off, nullptr, nullptr, DCP_OUT_F32, 0,
                  workspace, workspace_bytes};

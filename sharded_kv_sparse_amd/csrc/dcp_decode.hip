@@ -226,7 +226,11 @@ void decode_kernel(const DecodeParams p) {
   // scaled magnitude is >= 2^-2 exactly, smaller ones to within 2^-10
   // (scaled), i.e. to ~2^-16 of max|q|.
   const int head = hblk * kHeadsPerBlock + hg * 16 + i16;
-  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + head) * kHeadDim;
+  // In the last head block of a head count that is not a multiple of 64, a
+  // head group past the last head loads no query (zeros) and stores nothing;
+  // its waves still copy rows and take part in every barrier and merge.
+  const bool active = hblk * kHeadsPerBlock + hg * 16 < H;
+  const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)row * H + (active ? head : 0)) * kHeadDim;
   [[maybe_unused]] bf16x8 qf[FP8 ? 1 : 18];
   [[maybe_unused]] i32x8 qhi[FP8 ? 5 : 1], qlo[FP8 ? 5 : 1];
   float z_scale = p.sm_scale_log2;     // multiplies the raw MFMA logit
@@ -238,7 +242,7 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int dim = 128 * s + 32 * g + 8 * u;
-        raw[s][u] = dim < kHeadDim ? *reinterpret_cast<const bf16x8*>(qrow + dim) : bf16x8{};
+        raw[s][u] = active && dim < kHeadDim ? *reinterpret_cast<const bf16x8*>(qrow + dim) : bf16x8{};
 #pragma unroll
         for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(bf16_to_f32(raw[s][u][j])));
       }
@@ -275,7 +279,7 @@ void decode_kernel(const DecodeParams p) {
         }
   } else {
 #pragma unroll
-    for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g);
+    for (int s = 0; s < 18; ++s) qf[s] = active ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * g) : bf16x8{};
 #pragma unroll
     for (int s = 0; s < 18; ++s) touch(qf[s]);
   }
@@ -625,7 +629,7 @@ void decode_kernel(const DecodeParams p) {
     }
   }
 
-  finish_block<NT>(p, row, shard, split, head, g, ts == 0, oacc, m_run, l_tot, smem, &s_flag);
+  finish_block<NT>(p, row, shard, split, head, g, ts == 0 && active, oacc, m_run, l_tot, smem, &s_flag);
 }
 
 template <bool FP8, bool DENSE, int NW, int TS>
@@ -638,21 +642,20 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
 
 template <bool FP8, bool DENSE>
 hipError_t launch_heads(const DecodeParams& p, hipStream_t stream) {
-  // heads per block = min(H, 64): four 16-head groups, or fewer groups with
-  // each 64-token tile's two 32-token halves shared between waves.
-  switch (p.heads) {
-    case 128:
-    case 64: return launch_one<FP8, DENSE, 4, 1>(p, stream);
-    case 32: return launch_one<FP8, DENSE, 4, 2>(p, stream);
-    case 16: return launch_one<FP8, DENSE, 2, 2>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+  // heads per block = min(H, 64): four 16-head groups (from 48 heads on;
+  // the last block of a count that is not a multiple of 64 leaves groups
+  // idle), or fewer groups with each tile's token halves shared between
+  // waves (16 and 32 heads).
+  if (p.heads % 16 != 0 || p.heads > 128) return hipErrorInvalidValue;
+  if (p.heads >= 48) return launch_one<FP8, DENSE, 4, 1>(p, stream);
+  if (p.heads == 32) return launch_one<FP8, DENSE, 4, 2>(p, stream);
+  return launch_one<FP8, DENSE, 2, 2>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, bool fp8, bool dense, hipStream_t stream) {
-  if (fp8 && (p.heads == 64 || p.heads == 128)) return launch_decode_fp8(p, dense, stream);
+  if (fp8 && p.heads >= 48) return launch_decode_fp8(p, dense, stream);
   if (fp8) return dense ? launch_heads<true, true>(p, stream) : launch_heads<true, false>(p, stream);
   return dense ? launch_heads<false, true>(p, stream) : launch_heads<false, false>(p, stream);
 }

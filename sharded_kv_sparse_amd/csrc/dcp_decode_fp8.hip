@@ -1,4 +1,4 @@
-// Step 2 (+ step 3 fused) for FP8 E4M3 KV with 64 or 128 gathered heads:
+// Step 2 (+ step 3 fused) for FP8 E4M3 KV with 48 to 128 gathered heads:
 // absorbed-weight MLA decode with LSE over one DCP shard's paged latent KV,
 // the shards' partials merged in the epilogue of the last block of a row.
 //
@@ -32,7 +32,8 @@
 // time, so the row addresses of the next tile are ready without a dependent
 // global load.
 //
-// Per wave: 16 heads (4 waves = 64 heads; 128 heads use two blocks).  Per
+// Per wave: 16 heads (4 waves = 64 heads; more heads use more blocks, the
+// waves of the last block past the last head idle).  Per
 // tile: 8 S tiles x (4 latent k-steps x 2 (hi, lo) + 1 RoPE k-step) + 32 dim
 // tiles x 3 (P' terms) = 168 MFMAs of 16x16x128.
 #include "dcp_device.h"
@@ -209,15 +210,22 @@ void decode_fp8_kernel(const DecodeParams p) {
   // places before a load's first use do not count the inline copies, so a
   // use after them would also wait for every copy of tile 0.)
   const int head = hblk * kHeadsPerBlock + wave * 16 + i16;
+  // In the last head block of a head count that is not a multiple of 64,
+  // the waves past the last head copy rows and take part in every barrier
+  // and merge, but load no query and store nothing of their own.
+  const bool active = hblk * kHeadsPerBlock + wave * 16 < H;
   constexpr int kQWaveBytes = 16 * kHeadDim * 2;
   DCP_LDS char* q_lds = smem + kStageBytes + wave * kQWaveBytes;
-  {
+  if (active) {
     const char* qw = static_cast<const char*>(p.q) +
                      ((size_t)row * H + hblk * kHeadsPerBlock + wave * 16) * kHeadDim * 2;
 #pragma unroll
     for (int i = 0; i < kQWaveBytes / 1024; ++i) dma16(qw + 1024 * i + 16 * lane, q_lds + 1024 * i);
   }
-  if (wave >= 2) wait_vmcnt<18>();     // the ids (the query stays in flight)
+  if (wave >= 2) {                     // the ids (the query stays in flight)
+    if (active) wait_vmcnt<18>();
+    else wait_vmcnt<0>();
+  }
   lds_barrier();
   TileIds ids0;
   ids0.id[0] = ring[dma_tok];
@@ -258,6 +266,14 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       raw_r[u] = *reinterpret_cast<const DCP_LDS bf16x8*>(qh + 2 * (512 + 16 * g + 8 * u));
+    if (!active) {                     // no query: zeros (its results are never stored)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[s][u] = bf16x8{};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) raw_r[u] = bf16x8{};
+    }
   }
 
   // ---- query: Q * 2^e as E4M3 hi + lo (e per head: the largest with
@@ -606,7 +622,7 @@ void decode_fp8_kernel(const DecodeParams p) {
     const WsPartial<kThreads, true> wsp(p, row, shard, split, head, g,
                                          l_fin > 0.f ? 1.0f / l_fin : 0.f, ex_ws);
     auto store_pair = [&](int pair) {
-      if (ws_early && !wsp.is_own(2 * pair)) {
+      if (ws_early && active && !wsp.is_own(2 * pair)) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) wsp.store(2 * pair + j, oacc[2 * pair + j]);
       }
@@ -674,7 +690,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   wait_vmcnt<0>();   // copies queued for tiles that turned out empty
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
-  finish_block<kThreads, true>(p, row, shard, split, head, g, true, oacc, m_run * c, l_tot, smem, &s_flag,
+  finish_block<kThreads, true>(p, row, shard, split, head, g, active, oacc, m_run * c, l_tot, smem, &s_flag,
                                ex_ws, pre_stored);
 }
 

@@ -82,7 +82,9 @@ def _sparse(L, **kw):
 
 def test_sparse_decode_argument_checks(L):
     assert _sparse(L, q=None) == INVALID
-    assert _sparse(L, heads=48) == UNSUPPORTED
+    assert _sparse(L, heads=40) == UNSUPPORTED                    # heads: a multiple of 16 ...
+    assert _sparse(L, heads=8) == UNSUPPORTED
+    assert _sparse(L, heads=144) == UNSUPPORTED                   # ... up to 128
     assert _sparse(L, heads=256) == UNSUPPORTED
     assert _sparse(L, n=0) == INVALID
     assert _sparse(L, n=17) == INVALID
@@ -121,7 +123,7 @@ def test_noalloc_decode_argument_checks(L):
     # the same host checks as the workspace entry point, then the scratch limit
     # (checked before the scratch is touched, so no GPU is needed here)
     assert _noalloc(L, q=None) == INVALID
-    assert _noalloc(L, heads=48) == UNSUPPORTED
+    assert _noalloc(L, heads=40) == UNSUPPORTED
     assert _noalloc(L, scale=0.0) == INVALID
     assert _noalloc(L, o=None, lse=None) == INVALID
     assert _noalloc(L, splits=40) == UNSUPPORTED
@@ -236,6 +238,8 @@ def test_prefill_argument_checks(L):
     assert L.dcp_prefill_workspace_size(37, 24, 1000) == bad
     assert L.dcp_prefill_workspace_size(-1, 16, 1000) == bad
     assert L.dcp_prefill_workspace_size(0, 16, 1000) == 0
+    for h in (48, 80, 112):                                              # leftover queries: one row of 16-48
+        assert 0 < L.dcp_prefill_workspace_size(37, h, 1000) < bad
     need = L.dcp_prefill_workspace_size(4, 16, 100000)                  # one row: split, workspace
     assert need > 0 and chunk(tokens=4, c=100000, ws_bytes=need - 1) == WS_SMALL
 
@@ -270,6 +274,8 @@ def test_workspace_size_rules(L):
     assert ws(0, -1, 64, 2, 64, 1, 0, 0, 1) == bad
     assert ws(1, 4, 64, 2, 64, 0, 0, 0, 1) == bad                      # dense needs a page size
     assert ws(0, 0, 64, 2, 64, 1, 0, 0, 1) == 0
+    assert ws(0, 4, 40, 2, 64, 1, 0, 0, 1) == bad                      # a head count the decode rejects
+    assert ws(0, 4, 48, 2, 64, 1, 0, 0, 1) not in (0, bad)
     assert ws(0, 64, 64, 4, 2048, 1, 1, 1, 0) == 0                     # partials, one split: none
     fused = ws(0, 64, 64, 4, 2048, 1, 1, 0, 1)
     # counters + one fp32 partial (O and LSE) per (row, shard, split, head)
@@ -289,8 +295,15 @@ def test_decode_splits_rules(L):
     assert sp(0, 8, 64, 4, 2048, 1, 0) == 4                           # 32 units: 4 splits of 128 tokens
     assert sp(0, 8, 64, 4, 2048, 1, 8) == 8                           # asked for
     assert sp(0, 8, 64, 4, 2048, 1, 17) == -1                         # 17 x 4 partials: too many to merge
+    # every multiple of 16 up to 128 is a supported head count
+    for h in range(16, 129, 16):
+        assert sp(0, 8, h, 4, 2048, 1, 0) >= 1
+        assert sp(1, 8, h, 4, 2048, 64, 0) >= 1
+    assert sp(0, 8, 40, 4, 2048, 1, 0) == -1
+    assert sp(0, 8, 144, 4, 2048, 1, 0) == -1
     # the workspace query plans the same splits
-    for args in [(0, 8, 64, 4, 2048, 1), (1, 32, 128, 8, 131072, 64), (0, 96, 32, 2, 2048, 1)]:
+    for args in [(0, 8, 64, 4, 2048, 1), (1, 32, 128, 8, 131072, 64), (0, 96, 32, 2, 2048, 1),
+                 (0, 8, 48, 4, 2048, 1), (1, 4, 112, 2, 4096, 64)]:
         s = sp(*args, 0)
         assert s >= 1
         assert L.dcp_decode_workspace_size(*args, s, 0, 1) == L.dcp_decode_workspace_size(*args, 0, 0, 1)

@@ -147,6 +147,14 @@ SPARSE_SMALL = [
     ("bf16", 16, 1, 200, 2000, 0, 2),
     ("fp8", 128, 2, 190, 4000, 11, 2),
     ("bf16", 128, 4, 190, 4000, 0, 2),
+    # head counts that are not a multiple of 64: the last head block's waves
+    # past the last head load no query and store nothing
+    ("fp8", 48, 2, 300, 4000, 5, 3),
+    ("bf16", 48, 3, 250, 3000, 0, 2),
+    ("fp8", 80, 4, 260, 5000, 9, 2),
+    ("bf16", 96, 2, 190, 3000, 4, 2),
+    ("fp8", 112, 3, 333, 4000, 0, 2),
+    ("bf16", 112, 1, 200, 2000, 2, 1),
 ]
 
 
@@ -175,15 +183,15 @@ def test_sparse_decode_splits(gpu, kv, splits):
     check_against_oracle(res, oracle_sparse(w), f"splits={splits}")
 
 
-@pytest.mark.parametrize("kv,splits", [("fp8", 8), ("fp8", 12), ("fp8", 20), ("fp8", 32),
-                                       ("bf16", 32)])
+@pytest.mark.parametrize("kv,splits", [("fp8", 8), ("fp8", 12), ("fp8", 20), ("fp8", 24), ("fp8", 25),
+                                       ("fp8", 32), ("bf16", 32)])
 def test_sparse_decode_many_partials(gpu, kv, splits):
-    # 16, 24, 40 or 64 partials per row (2 shards x splits): the merge's wide
-    # load groups (16 or 32 members per pass, several groups), two rounds of
-    # LSE loads, abandon bits above bit 31 of the arrival word (40 members
-    # merging in parallel), rows merged by their last block alone (64
-    # partials, more than the 56 abandon bits), and empty splits; merged and
-    # per-shard outputs within tolerance
+    # 16, 24, 40, 48, 50 or 64 partials per row (2 shards x splits): the
+    # merge's wide load groups (16 or 32 members per pass, several groups),
+    # two rounds of LSE loads, abandon bits above bit 31 of the arrival word
+    # (40 and 48 members merging in parallel, 48 the most that have abandon
+    # bits), rows merged by their last block alone (50 and 64 partials), and
+    # empty splits; merged and per-shard outputs within tolerance
     p = wl.Preset("t", "sparse", kv, batch=2, q_per_seq=1, heads=64, context=40000, num_shards=2,
                   topk=8000, pad_tail=300, seed=60 + splits)
     w = make(p)
@@ -358,6 +366,10 @@ DENSE_SMALL = [
     ("fp8", 128, 8, 5000, 64, 4, True),
     ("fp8", 32, 2, 777, 128, 3, False),
     ("bf16", 32, 1, 1000, 64, 2, False),
+    ("fp8", 48, 2, 1500, 64, 2, True),
+    ("bf16", 80, 3, 1200, 64, 2, False),
+    ("fp8", 96, 4, 2100, 16, 2, False),
+    ("fp8", 112, 2, 900, 64, 3, False),
 ]
 
 

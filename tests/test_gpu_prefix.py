@@ -74,6 +74,8 @@ CHUNK_CASES = [
     ("fp8", 16, 37, 1000), ("fp8", 32, 33, 700), ("fp8", 64, 9, 1300), ("fp8", 128, 5, 900),
     ("bf16", 16, 37, 1000), ("bf16", 32, 20, 333), ("bf16", 64, 8, 700), ("bf16", 128, 3, 260),
     ("fp8", 16, 64, 1), ("fp8", 16, 8, 0), ("bf16", 32, 6, 0), ("fp8", 16, 3, 5000),
+    # (token, head) queries left over after the rows of 64: 16, 32, 48 and 48
+    ("fp8", 48, 7, 900), ("bf16", 96, 5, 500), ("fp8", 80, 3, 1100), ("bf16", 112, 1, 300),
 ]
 
 
