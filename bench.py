@@ -308,7 +308,7 @@ def measure_prefill(stream, dev, reps=20, name="prefill_fp8_prefix16k_new2k"):
         "gather": {"kernel": "gather_prefix_kernel", "us_per_chunk": round(per[0], 2),
                    "gbps": round(g_bytes / (per[0] * 1e-6) / 1e9, 1),
                    "frac_hbm_peak": round(g_bytes / (per[0] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "attention": {"kernel": ("decode_fp8_kernel<true>" if fp8 and heads * tokens % 64 == 0
+        "attention": {"kernel": ("decode_fp8_kernel<true, false>" if fp8 and heads * tokens % 64 == 0
                                  else "decode_kernel") + " (dense, one contiguous chunk)",
                       "us_per_chunk": round(per[1], 2),
                       "tflops": round(a_flops / (per[1] * 1e-6) / 1e12, 1),

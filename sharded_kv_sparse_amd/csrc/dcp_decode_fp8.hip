@@ -66,7 +66,9 @@ __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, h, true);
 }
 
-template <bool DENSE>
+// PARTIAL: the head count is not a multiple of 64 (the last head block has
+// idle waves).
+template <bool DENSE, bool PARTIAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_fp8_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
@@ -213,7 +215,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   // In the last head block of a head count that is not a multiple of 64,
   // the waves past the last head copy rows and take part in every barrier
   // and merge, but load no query and store nothing of their own.
-  const bool active = hblk * kHeadsPerBlock + wave * 16 < H;
+  const bool active = !PARTIAL || hblk * kHeadsPerBlock + wave * 16 < H;
   constexpr int kQWaveBytes = 16 * kHeadDim * 2;
   DCP_LDS char* q_lds = smem + kStageBytes + wave * kQWaveBytes;
   if (active) {
@@ -699,7 +701,11 @@ void decode_fp8_kernel(const DecodeParams p) {
 hipError_t launch_decode_fp8(const DecodeParams& p, bool dense, hipStream_t stream) {
   const long long blocks = p.rows * p.num_shards * (long long)p.num_splits * p.head_blocks;
   void* args[] = {(void*)&p};
-  const void* fn = dense ? (const void*)decode_fp8_kernel<true> : (const void*)decode_fp8_kernel<false>;
+  const bool partial = p.heads % kHeadsPerBlock != 0;
+  const void* fn = dense ? (partial ? (const void*)decode_fp8_kernel<true, true>
+                                    : (const void*)decode_fp8_kernel<true, false>)
+                         : (partial ? (const void*)decode_fp8_kernel<false, true>
+                                    : (const void*)decode_fp8_kernel<false, false>);
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, stream);
 }
 
