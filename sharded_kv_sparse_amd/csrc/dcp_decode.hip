@@ -20,14 +20,15 @@
 // Inside a block, wave w owns 16 heads (head group hg) and, when the block
 // has fewer than four head groups, a share of each tile's tokens (token
 // group ts).  Per tile:
-//   * the KV rows of 64 tokens (36 KB FP8, three stages; 72 KB BF16, two
-//     stages) are copied straight from HBM into LDS with global->LDS DMA,
+//   * the KV rows of a tile (64 tokens FP8, 32 tokens BF16: 36 KB either
+//     way, four stages) are copied straight from HBM into LDS with global->LDS DMA,
 //     granule-major (each copy instruction moves one 64-byte granule of 16
 //     tokens, so a lane keeps one token, and one id, for all its copies of
 //     a tile), chunks swizzled against bank conflicts; the tile's slot or
 //     page ids arrive two tiles ahead in an LDS ring, by the same DMA;
-//   * S^T = K Q^T on bf16 MFMA 16x16x32 (K codes converted to bf16 after the
-//     LDS read -- E4M3 is exact in bf16; Q stays in registers for the block);
+//   * S^T = K Q^T: FP8 KV on the fp8 MFMA 16x16x128 (block-scaled), the K
+//     codes straight from LDS and Q * 2^e split into E4M3 hi + lo; BF16 KV on
+//     the bf16 MFMA 16x16x32; Q stays in registers for the block;
 //   * online softmax in base 2, row statistics kept per head = per lane
 //     column, reductions over the four lanes of a head with shuffles;
 //   * O^T += V^T P^T: V^T operands come straight out of the row-major tile
@@ -35,9 +36,11 @@
 //     fp16 MFMA with P' = p * per-token scale in fp16 (V codes exact in fp16).
 //     BF16: bf16 MFMA twice, P split into bf16 hi + lo.
 // Epilogue: O / l and LSE = ln(sum) per head; partials go to o_part and/or
-// the workspace; an arrival counter per (row) [and per (row, shard) when a
-// shard is split] elects the last block, which merges the partials with LSE
-// weights and resets the counter for the next call.
+// the workspace.  An arrival word per (row, head block) [and a counter per
+// (row, shard, head block) when a shard is split] orders the merge with LSE
+// weights: when the whole grid is resident, the row's blocks wait for each
+// other and each merges a share of the row, else the last block to arrive
+// merges it; either way the word is left ready for the next call.
 #include "dcp_device.h"
 #include "dcp_epilogue.h"
 #include "dcp_internal.h"
