@@ -58,7 +58,7 @@ struct DecodeParams {
   float* ws_o;                   // [rows, N, S, heads, 512]
   float* ws_lse;                 // [rows, N, S, heads]
   int* ws_exp;                   // [rows, N, S, heads]: power of two of an fp16 row-merge partial
-  int* cnt_row;                  // [rows, head blocks, 4]: 64-bit arrival word, completion word
+  int* cnt_row;                  // [rows, head blocks, 4]: 64-bit arrival word (two words spare)
   int* cnt_shard;                // [rows, N, head blocks]
   int xcd_swizzle;               // grid is a multiple of 8: keep a row's blocks on one XCD
   int merge_wait_ticks;          // >0: blocks wait up to this many 100 MHz ticks to share a merge
