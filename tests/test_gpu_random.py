@@ -1,6 +1,7 @@
 """GPU parity on seeded random configurations: head count, shard count,
 splits, KV dtype and layout, page size, row lengths and output options drawn
-together, so that combinations the fixed cases do not name are checked too.
+together (and, for the prefill chunk attention, token count, head count and
+chunk length), so that combinations the fixed cases do not name are checked.
 Same bar as the fixed cases: remap bit-exact, max |dO| <= 1e-2 and max |dLSE|
 <= 1e-3 against the fp64 oracle, -inf matched exactly, no NaN.
 """
@@ -9,10 +10,13 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from sharded_kv_sparse_amd import binding as B
 from sharded_kv_sparse_amd import workloads as wl
 
-from ._support import check_against_oracle, gpu_dense, gpu_sparse, make, oracle_dense, oracle_sparse
+from ._support import (assert_attn_close, check_against_oracle, gpu_dense, gpu_sparse, make, oracle_dense,
+                       oracle_sparse, to_np)
+from .test_gpu_prefix import _chunk, _chunk_host
 
 
 def draw_case(seed):
@@ -46,7 +50,7 @@ def draw_case(seed):
     return p, splits, want_partials, want_merged, out_dtype
 
 
-SEEDS = list(range(9001, 9025))
+SEEDS = list(range(9001, 9049))
 
 
 def test_random_cases_are_varied():
@@ -81,3 +85,27 @@ def test_random_configuration(gpu, seed):
         ref = oracle_dense(w)
     assert ("o_part" in res) == want_partials and ("o" in res) == want_merged
     check_against_oracle(res, ref, f"random seed={seed}")
+
+
+PREFILL_SEEDS = list(range(9101, 9117))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", PREFILL_SEEDS)
+def test_random_prefill_chunk(gpu, seed):
+    rng = np.random.default_rng(seed)
+    kv = "fp8" if rng.random() < 0.5 else "bf16"
+    heads = int(rng.integers(1, 9)) * 16
+    tokens = int(rng.integers(1, 81))
+    c = int(rng.integers(0, 3001))
+    print(f"[gpu-case] random prefill seed={seed} {kv} H={heads} T={tokens} C={c}", flush=True)
+    rows, sc = _chunk(kv, c, seed=seed)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed + 500000)        # independent of the chunk's draw
+    q = torch.randn((tokens, heads, 576), generator=gen, device="cuda").to(torch.bfloat16)
+    o, lse = B.prefill_chunk_attention(q, rows, sc, 1.0 / np.sqrt(192.0))
+    torch.cuda.synchronize()
+    hr, hs = _chunk_host(kv, rows, sc)
+    qh = oracle.decode_bf16(q.cpu().view(torch.int16).numpy().view(np.uint16))
+    o_ref, lse_ref = oracle.prefix_chunk_attention(qh, hr, hs, kv, 1.0 / np.sqrt(192.0))
+    assert_attn_close(to_np(o), to_np(lse), o_ref, lse_ref, f"random prefill seed={seed}")
