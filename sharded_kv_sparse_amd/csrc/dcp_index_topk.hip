@@ -16,10 +16,12 @@
 // key codes k_t and scale s_t > 0,
 //     score(t) = s_t * sum_h w_h * max(0, q_h . k_t),
 // with q_h . k_t on the fp8 MFMA (16 tokens x 16 heads x 128 dims per
-// instruction; every product of two E4M3 values is exact, the sums fp32).
-// One wave scores 64 tokens (four 16-token groups); its A operands come
-// straight from global memory (a token's 128-byte key row is one line, and
-// the 16 tokens of a group are contiguous rows of a page).
+// instruction; every product of two E4M3 values is exact, and the
+// instruction's sum keeps about 14 bits below its largest product).
+// One wave scores 256 tokens, sixteen 16-token groups loaded four at a time;
+// its A operands come straight from global memory (a token's 128-byte key
+// row is one line, and the 16 tokens of a group are contiguous rows of a
+// page).  The sum over a group's 16 heads runs on DPP row moves.
 //
 // Selection: score descending, then position ascending, as one 64-bit key
 // (the order-preserving image of the fp32 score above the complement of the
@@ -35,12 +37,29 @@ namespace {
 
 constexpr int kScoreThreads = 256;                 // 4 waves
 constexpr int kScoreWaveGroups = 16;               // 16-token groups per wave
-constexpr int kScoreBatch = 8;                     // groups loaded together
+constexpr int kScoreBatch = 4;                     // groups loaded together
 constexpr int kScoreTokens = 4 * 16 * kScoreWaveGroups;   // 1024 tokens per block
 constexpr int kSelectThreads = 1024;
 
 // ---------------------------------------------------------------- scores
 
+// Sum over the 16 lanes of each row of the wave (every lane gets its row's
+// sum): the quads first, then the row's half mirror and full mirror, all by
+// DPP moves (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_move<0xb1>(x);     // quad_perm 1,0,3,2
+  x += dpp_move<0x4e>(x);     // quad_perm 2,3,0,1
+  x += dpp_move<0x141>(x);    // row_half_mirror: quad 0 <-> 1, 2 <-> 3
+  x += dpp_move<0x140>(x);    // row_mirror: the two halves
+  return x;
+}
+
+// HG: index head groups of 16.
+template <int HG>
 __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(IndexScoreParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
@@ -61,21 +80,15 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(IndexScorePa
   typedef __attribute__((ext_vector_type(4))) int i32x4_t;
   const unsigned char* qrow = p.q + (size_t)row * p.hi * kIndexDim;
   const float* wrow = p.w + (size_t)row * p.hi;
-  const int HG = p.hi / 16;
-  i32x8 qb[kMaxIndexHeads / 16];
-  float wv[kMaxIndexHeads / 16];
+  i32x8 qb[HG];
+  float wv[HG];
 #pragma unroll
-  for (int hg = 0; hg < kMaxIndexHeads / 16; ++hg) {
-    if (hg < HG) {
-      const unsigned char* qh = qrow + (size_t)(16 * hg + i16) * kIndexDim;
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(qh + 16 * g);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(qh + 64 + 16 * g);
-      qb[hg] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      wv[hg] = wrow[16 * hg + i16];
-    } else {
-      qb[hg] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      wv[hg] = 0.f;
-    }
+  for (int hg = 0; hg < HG; ++hg) {
+    const unsigned char* qh = qrow + (size_t)(16 * hg + i16) * kIndexDim;
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(qh + 16 * g);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(qh + 64 + 16 * g);
+    qb[hg] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    wv[hg] = wrow[16 * hg + i16];
   }
   const int* bt = p.block_table + row * p.max_pages;
   const long long max_prow = sh.pool_rows - 1;
@@ -108,19 +121,15 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(IndexScorePa
       // lane (head i16, g): tokens 4g .. 4g + 3 of the group, summed over head groups
       f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hg = 0; hg < kMaxIndexHeads / 16; ++hg) {
-        if (hg < HG) {
-          const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              ka[u], qb[hg], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+      for (int hg = 0; hg < HG; ++hg) {
+        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            ka[u], qb[hg], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part[i] += wv[hg] * fmaxf(d[i], 0.f);
-        }
+        for (int i = 0; i < 4; ++i) part[i] += wv[hg] * fmaxf(d[i], 0.f);
       }
-      // sum over the 16 heads of the group's lanes (xor over lane bits 0..3)
+      // sum over the 16 heads of the group's lanes
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], m, 64);
+      for (int i = 0; i < 4; ++i) part[i] = row16_sum(part[i]);
       // token 4g + i's scale sits in lane 4g + i (its A row)
       f32x4 res;
 #pragma unroll
@@ -532,8 +541,19 @@ hipError_t launch_topk_merge(const TopkParams& p, long long rows, hipStream_t st
 hipError_t launch_index_score(const IndexScoreParams& p, hipStream_t stream) {
   const long long blocks = p.rows * p.num_shards * (long long)p.tiles_per_list;
   void* args[] = {(void*)&p};
-  return hipLaunchKernel((const void*)index_score_kernel, dim3((unsigned)blocks), dim3(kScoreThreads),
-                         args, 0, stream);
+  const void* fn;
+  switch (p.hi / 16) {
+    case 1: fn = (const void*)index_score_kernel<1>; break;
+    case 2: fn = (const void*)index_score_kernel<2>; break;
+    case 3: fn = (const void*)index_score_kernel<3>; break;
+    case 4: fn = (const void*)index_score_kernel<4>; break;
+    case 5: fn = (const void*)index_score_kernel<5>; break;
+    case 6: fn = (const void*)index_score_kernel<6>; break;
+    case 7: fn = (const void*)index_score_kernel<7>; break;
+    case 8: fn = (const void*)index_score_kernel<8>; break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kScoreThreads), args, 0, stream);
 }
 
 hipError_t launch_topk_select(const TopkParams& p, long long lists, hipStream_t stream) {
