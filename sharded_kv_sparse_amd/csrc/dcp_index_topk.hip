@@ -320,7 +320,7 @@ __device__ __forceinline__ void hist_add(unsigned* hist, unsigned bin, bool on) 
 }
 
 __global__ __launch_bounds__(kSelectThreads) void topk_local_fast_kernel(TopkParams p) {
-  __shared__ unsigned hist[256];
+  __shared__ unsigned whist[kSelectThreads / 64][256];   // one digit histogram per wave
   __shared__ unsigned s_word[4];
   __shared__ unsigned wave_sum[kSelectThreads / 64];
   __shared__ unsigned long long sel[kMaxTopk];
@@ -345,24 +345,48 @@ __global__ __launch_bounds__(kSelectThreads) void topk_local_fast_kernel(TopkPar
   if (n > k) {
     unsigned prefix = 0u, mask = 0u, rem = (unsigned)k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0u;
-      __syncthreads();
+      // each wave counts its own keys (no atomics across waves); the wave's
+      // LDS operations stay in order, so its zeroing needs no barrier
+#pragma unroll
+      for (int j = 0; j < 4; ++j) whist[wv][4 * lane + j] = 0u;
 #pragma unroll
       for (int i = 0; i < kLocalVpt; ++i) {
         const int e = tid + i * kSelectThreads;
-        hist_add(hist, (key[i] >> shift) & 255u, e < n && (key[i] & mask) == prefix);
+        hist_add(whist[wv], (key[i] >> shift) & 255u, e < n && (key[i] & mask) == prefix);
       }
       __syncthreads();
-      if (tid == 0) {
-        unsigned above = 0u;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (above + hist[d] >= rem) break;
-          above += hist[d];
+      // wave 0: lane l sums bins 4l .. 4l + 3 over the waves; the bucket d of
+      // the rem-th largest key is the largest d whose suffix count S(d) =
+      // sum of bins >= d reaches rem (S(0) >= rem, S(256) = 0 < rem, so
+      // exactly one lane holds it)
+      if (wv == 0) {
+        unsigned c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          unsigned t = 0u;
+#pragma unroll
+          for (int w = 0; w < kSelectThreads / 64; ++w) t += whist[w][4 * lane + j];
+          c[j] = t;
         }
-        s_word[0] = prefix | ((unsigned)d << shift);
-        s_word[1] = rem - above;              // still to take from bucket d
-        s_word[2] = hist[d];                  // bucket d's size
+        const unsigned mine = c[0] + c[1] + c[2] + c[3];
+        unsigned suf = mine;                  // bins >= 4 lane
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const unsigned t = __shfl_down(suf, o, 64);
+          if (lane + o < 64) suf += t;
+        }
+        unsigned above = suf - mine;          // S(4 lane + 4)
+        if (suf >= rem && above < rem) {
+          int j = 3;
+          for (; j > 0; --j) {
+            if (above + c[j] >= rem) break;
+            above += c[j];
+          }
+          const int d = 4 * lane + j;
+          s_word[0] = prefix | ((unsigned)d << shift);
+          s_word[1] = rem - above;            // still to take from bucket d
+          s_word[2] = c[j];                   // bucket d's size
+        }
       }
       __syncthreads();
       prefix = s_word[0];
