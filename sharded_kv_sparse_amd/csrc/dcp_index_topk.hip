@@ -478,16 +478,20 @@ __global__ __launch_bounds__(kSelectThreads) void topk_local_fast_kernel(TopkPar
 // selection order, padding last) are staged in LDS as keys; an element's
 // place in the merged order is its index in its own list plus, for every
 // other list, the number of that list's keys above it (a binary search; keys
-// are distinct).  Elements whose place is below k are written there.
+// are distinct).  Elements whose place is below k are written there.  Four
+// blocks share a row: each stages all of the row's keys and places a fourth
+// of them.
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeMaxKeys = 8192;                 // num_shards * k staged in LDS
-constexpr int kMergeRun = kMergeMaxKeys / kMergeThreads;   // consecutive elements per thread
+constexpr int kMergeParts = 4;                     // blocks per row, each placing a fourth of the elements
+constexpr int kMergeRun = kMergeMaxKeys / (kMergeThreads * kMergeParts);   // consecutive elements per thread
 
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_rank_kernel(TopkParams p) {
   __shared__ unsigned long long keys[kMergeMaxKeys];
   __shared__ int s_valid;
   const int tid = threadIdx.x;
-  const long long row = blockIdx.x;
+  const long long row = blockIdx.x / kMergeParts;
+  const int part = (int)(blockIdx.x % kMergeParts);
   const int K = p.k_in, N = p.num_shards, k = p.k;
   if (tid == 0) s_valid = 0;
   __syncthreads();
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_rank_kernel(TopkPara
   // Each thread takes kMergeRun consecutive elements of one list (descending
   // keys): the first one's count in every other list by binary search, the
   // next ones by walking on from the previous count (counts only grow).
-  const int e0 = tid * kMergeRun;
+  const int e0 = (part * kMergeThreads + tid) * kMergeRun;
   int cnt[kMaxShards];
   for (int e = e0; e < min(e0 + kMergeRun, N * K); ++e) {
     const unsigned long long kv = keys[e];
@@ -544,7 +548,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_rank_kernel(TopkPara
       }
     }
   }
-  for (int i = m + tid; i < k; i += kMergeThreads) {
+  for (int i = m + part * kMergeThreads + tid; i < k; i += kMergeThreads * kMergeParts) {
     if (p.out_score) p.out_score[row * k + i] = kNegInf;
     if (p.out_pos) p.out_pos[row * k + i] = -1;
     if (p.out_slot) p.out_slot[row * k + i] = -1;
@@ -558,7 +562,7 @@ hipError_t launch_topk_merge(const TopkParams& p, long long rows, hipStream_t st
   if ((long long)p.num_shards * p.k_in > kMergeMaxKeys)
     return hipLaunchKernel((const void*)topk_select_kernel, dim3((unsigned)rows), dim3(kSelectThreads),
                            args, 0, stream);
-  return hipLaunchKernel((const void*)topk_merge_rank_kernel, dim3((unsigned)rows), dim3(kMergeThreads),
+  return hipLaunchKernel((const void*)topk_merge_rank_kernel, dim3((unsigned)(rows * kMergeParts)), dim3(kMergeThreads),
                          args, 0, stream);
 }
 
