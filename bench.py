@@ -137,7 +137,7 @@ def flops(p, tokens):
 
 
 def fp8_kernel_mfma(p, w, splits):
-    """MFMAs the FP8 decode kernel (64 or 128 heads) executes for one launch.
+    """MFMAs the FP8 decode kernel (48 to 128 heads) executes for one launch.
 
     Per wave (16 heads) and 128-token tile: 8 S tiles x (4 latent k-steps x 2
     query terms + 1 RoPE k-step) + 32 dim tiles x 3 P' terms = 168; a tile of

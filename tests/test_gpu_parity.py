@@ -236,7 +236,7 @@ def test_fp8_large_token_scales(gpu, heads):
     # values, at most 4, and the logits stay moderate): P' = p * scale reaches
     # 2^19, beyond fp16, so the 16/32-head kernel must scale P' per head before
     # converting it to fp16.  Partials and the merge within tolerance of the
-    # oracle.  (The 64/128-head kernel has no fp16 P': it splits P' into E4M3
+    # oracle.  (The kernel for 48 heads or more has no fp16 P': it splits P' into E4M3
     # terms at a power of two per head, whose 17 binades cover the P' that
     # carry the output as long as a token's scale is not thousands of times
     # what its codes need, which this construction is on purpose.)
