@@ -530,7 +530,9 @@ void decode_fp8_kernel(const DecodeParams p) {
     // The token scales are read from LDS twice rather than kept in registers.
     float z[NS][4];
     float tmax = kNegInf;
-    const bool full = tok0 + kT <= tend;
+    // Only the short lead tile and the last tile can be partial: every other
+    // tile holds kT valid tokens (the lead takes the remainder up front).
+    const bool full = (next && !first_short) || tok0 + kT <= tend;
 #pragma unroll
     for (int st = 0; st < NSS; ++st) {
       const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
