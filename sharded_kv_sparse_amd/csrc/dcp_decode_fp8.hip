@@ -53,6 +53,7 @@ constexpr int kSmem = kRingOff + 3 * kT * 4;       // 150016 bytes
 constexpr int kThreads = 256;
 
 template <bool B> struct BoolC { static constexpr bool value = B; };
+template <int V> struct IntC { static constexpr int value = V; };
 
 // The page table of a prefill chunk: one page, id 0, holding the whole chunk.
 __device__ int kChunkPage[1] = {0};
@@ -393,9 +394,11 @@ void decode_fp8_kernel(const DecodeParams p) {
   // The last tile, when at most 64 of its tokens are valid ("short"),
   // skips the QK pass over S tiles 4..7 and packs the three P' terms of its
   // 64 tokens into the k slots of two MFMAs per dim tile instead of three.
-  auto tile = [&](auto next_c, auto first_c, int it) {
+  auto tile = [&](auto next_c, auto lead_c, int it) {
     constexpr bool next = decltype(next_c)::value;
-    constexpr bool first_short = decltype(first_c)::value;   // the short lead tile
+    // the lead tile: 33..64 tokens ("short") or 1..32 ("tiny")
+    constexpr bool first_short = decltype(lead_c)::value > 0;
+    constexpr bool first_tiny = decltype(lead_c)::value == 2;
     constexpr int NS = 8, NQ = 4, NH = 2;
     wait_vmcnt<10>();
     lds_barrier();                       // granules 0..3 of tile it, its scales, ring(it + 1)
@@ -435,6 +438,8 @@ void decode_fp8_kernel(const DecodeParams p) {
         }
         break;
       }
+      // S tiles of this pass (a tiny lead tile's tokens all sit in S tiles 0, 1)
+      const int nq = (half == 0 && first_tiny) ? 2 : NQ;
       f32x4 acc[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -456,7 +461,8 @@ void decode_fp8_kernel(const DecodeParams p) {
       // first operands.)
       if (half == 0) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) a[q] = load_kq(0, 0, q);
+        for (int q = 0; q < NQ; ++q)
+          if (q < nq) a[q] = load_kq(0, 0, q);
       }
       const bool more = half == 0 && !short_tile;
 #pragma unroll
@@ -476,6 +482,7 @@ void decode_fp8_kernel(const DecodeParams p) {
         if (s < 4) {
 #pragma unroll
           for (int q = 0; q < NQ; q += 2) {
+            if (q >= nq) break;
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qhi[s], acc[q], 0, 0, 0, 127, 0, qscale);
             acc[q + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q + 1], qhi[s], acc[q + 1], 0, 0, 0, 127, 0, qscale);
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qlo[s], acc[q], 0, 0, 0, 127, 0, qscale);
@@ -487,6 +494,7 @@ void decode_fp8_kernel(const DecodeParams p) {
           // one MFMA, q + 1's next operand
 #pragma unroll
           for (int q = 0; q < NQ; q += 2) {
+            if (q >= nq) break;
             __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -495,6 +503,7 @@ void decode_fp8_kernel(const DecodeParams p) {
         } else {
 #pragma unroll
           for (int q = 0; q < NQ; ++q) {
+            if (q >= nq) break;
             acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q], qr, acc[q], 0, 0, 0, 127, 0, qscale);
             if (more) a[q] = load_kq(1, 0, q);
           }
@@ -511,9 +520,10 @@ void decode_fp8_kernel(const DecodeParams p) {
 
     // First V^T operands, read before the softmax so their latency hides.
     // The short lead tile's 64 tokens need only the first two tr8 reads of a
-    // dim tile, and its softmax only the first four S tiles.
-    constexpr int NR = first_short ? 2 : 4;        // tr8 reads per dim tile
-    constexpr int NSS = first_short ? 4 : NS;      // S tiles the softmax covers
+    // dim tile, and its softmax only the first four S tiles; the tiny one's
+    // 32 tokens one read and two S tiles.
+    constexpr int NR = first_tiny ? 1 : first_short ? 2 : 4;        // tr8 reads per dim tile
+    constexpr int NSS = first_tiny ? 2 : first_short ? 4 : NS;      // S tiles the softmax covers
     i32x2 vr[2][2][NR];
     auto load_v = [&](int d, i32x2* r4) {
 #pragma unroll
@@ -527,15 +537,19 @@ void decode_fp8_kernel(const DecodeParams p) {
     // ---- online softmax over the tile (lane: tokens 16st + 4g + i).  The
     // reference max only moves when the tile max exceeds it by more than 8
     // (base 2), so O and l are rescaled rarely; p stays <= 2^8.
-    // The token scales are read from LDS twice rather than kept in registers.
+    // The token scales are read from LDS once, all together, and kept in
+    // registers for both passes.
     float z[NS][4];
     float tmax = kNegInf;
     // Only the short lead tile and the last tile can be partial: every other
     // tile holds kT valid tokens (the lead takes the remainder up front).
     const bool full = (next && !first_short) || tok0 + kT <= tend;
+    f32x4 s4v[NSS];
+#pragma unroll
+    for (int st = 0; st < NSS; ++st) s4v[st] = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
 #pragma unroll
     for (int st = 0; st < NSS; ++st) {
-      const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
+      const f32x4 s4 = s4v[st];
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[st][i] = sacc[st][i] * s4[i];
     }
@@ -569,7 +583,7 @@ void decode_fp8_kernel(const DecodeParams p) {
     float pmax = 0.f;
 #pragma unroll
     for (int st = 0; st < NSS; ++st) {
-      const f32x4 s4 = *reinterpret_cast<const DCP_LDS f32x4*>(sb + sc_off + 64 * st);
+      const f32x4 s4 = s4v[st];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = fast_exp2(fmaf(z[st][i], c, neg_mc));
@@ -608,7 +622,7 @@ void decode_fp8_kernel(const DecodeParams p) {
       pb[0][st] = h;
       pb[1][st] = m;
       pb[2][st] = l;
-      if (st == 2) copy_at(12);
+      if (st == (NSS > 2 ? 2 : NSS - 1)) copy_at(12);
       if (st == (NSS > 5 ? 5 : NSS - 1)) copy_at(13);
     }
 
@@ -616,8 +630,10 @@ void decode_fp8_kernel(const DecodeParams p) {
     // dim-tile pair right behind its final MFMAs.  l is complete once the
     // softmax has run, and |O / l| <= 448 * (largest token scale), since O / l
     // is a convex combination of scaled E4M3 values: that bound fixes the
-    // fp16 exponent before O is known.
-    const bool ws_early = !next && (p.o != nullptr || (p.o_part != nullptr && p.num_splits > 1));
+    // fp16 exponent before O is known.  (Only the fp16 partial of the row
+    // merge is stored early; the fp32 one of a split shard is stored after
+    // the loop.)
+    const bool ws_early = !next && p.o != nullptr && !(p.o_part != nullptr && p.num_splits > 1);
     if constexpr (!next) {
       l_fin = sum_xor32(sum_xor16(l_run));
       ex_ws = half_exponent(448.0f * max_xor32(max_xor16(smax)));
@@ -625,10 +641,14 @@ void decode_fp8_kernel(const DecodeParams p) {
     }
     const WsPartial<kThreads, true> wsp(p, row, shard, split, head, g,
                                          l_fin > 0.f ? 1.0f / l_fin : 0.f, ex_ws);
+    // No branch per store: the own dim tiles (kept in registers for the
+    // merge) and an idle wave's tiles are stored past the end of the
+    // workspace resource, where the store is dropped.
     auto store_pair = [&](int pair) {
-      if (ws_early && active && !wsp.is_own(2 * pair)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) wsp.store(2 * pair + j, oacc[2 * pair + j]);
+      for (int j = 0; j < 2; ++j) {
+        const int d = 2 * pair + j;
+        wsp.store_half(d, oacc[d], active && !wsp.is_own(d));
       }
     };
 
@@ -636,11 +656,17 @@ void decode_fp8_kernel(const DecodeParams p) {
     // k slot byte 4st + i of lane group g is token 16st + 4g + i, one MFMA
     // per P' term.  A short tile's 64 tokens sit in bytes 0..15 (tr8 reads
     // 0, 1); its operands repeat them, with the terms (hi, mid) in one MFMA
-    // and (lo, zero) in a second.
-    auto pv = [&](auto short_c) {
+    // and (lo, zero) in a second.  A tiny lead tile's 32 tokens sit in bytes
+    // 0..7 (tr8 read 0): hi, mid and lo go into bytes 0..23 of one MFMA.
+    auto pv = [&](auto short_c, auto store_c) {
       constexpr bool sh = decltype(short_c)::value;
+      constexpr bool st = decltype(store_c)::value;   // the last tile's early stores
+      constexpr bool ty = first_tiny;                 // all three terms in one MFMA
+      constexpr int NT3 = ty ? 1 : sh ? 2 : 3;        // MFMAs per dim tile
       i32x8 pf[2];
-      if constexpr (sh) {
+      if constexpr (ty) {
+        pf[0] = i32x8{pb[0][0], pb[0][1], pb[1][0], pb[1][1], pb[2][0], pb[2][1], 0, 0};
+      } else if constexpr (sh) {
         pf[0] = i32x8{pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
         pf[1] = i32x8{pb[2][0], pb[2][1], pb[2][2], pb[2][3], 0, 0, 0, 0};
       }
@@ -654,7 +680,9 @@ void decode_fp8_kernel(const DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const i32x2* r4 = vr[grp & 1][j];
-          if constexpr (sh)
+          if constexpr (ty)
+            vt[j] = i32x8{r4[0].x, r4[0].y, r4[0].x, r4[0].y, r4[0].x, r4[0].y, r4[0].x, r4[0].y};
+          else if constexpr (sh)
             vt[j] = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[0].x, r4[0].y, r4[1].x, r4[1].y};
           else
             vt[j] = i32x8{r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[NR - 2].x, r4[NR - 2].y, r4[NR - 1].x, r4[NR - 1].y};
@@ -664,33 +692,42 @@ void decode_fp8_kernel(const DecodeParams p) {
         }
         // term-major: two independent accumulators between dependent MFMAs
 #pragma unroll
-        for (int term = 0; term < (sh ? 2 : 3); ++term)
+        for (int term = 0; term < NT3; ++term)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             oacc[2 * grp + j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                vt[j], sh ? pf[term] : pb[term], oacc[2 * grp + j], 0, 0, 0, 127, 0, pscale);
-        if constexpr (!next) {
+                vt[j], (ty || sh) ? pf[term] : pb[term], oacc[2 * grp + j], 0, 0, 0, 127, 0, pscale);
+        if constexpr (st) {
           if (grp > 0) store_pair(grp - 1);
         }
         // issue order: the next pair's V^T reads first, then this pair's MFMAs
         if (grp + 1 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, sh ? 4 : 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NT3, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (!next) store_pair(15);
+      if constexpr (st) store_pair(15);
     };
-    if constexpr (first_short) {
-      pv(BoolC<true>{});
+    auto run_pv = [&](auto store_c) {
+      if constexpr (first_short) {
+        pv(BoolC<true>{}, store_c);
+      } else {
+        if (!short_tile) pv(BoolC<false>{}, store_c);
+        else pv(BoolC<true>{}, store_c);
+      }
+    };
+    if constexpr (next) {
+      run_pv(BoolC<false>{});
     } else {
-      if (!short_tile) pv(BoolC<false>{});
-      else pv(BoolC<true>{});
+      if (ws_early) run_pv(BoolC<true>{});
+      else run_pv(BoolC<false>{});
     }
   };
   // Tile 0's copies are waited for at its top like any tile's.
   int it = 0;
-  if (lead > 0) tile(BoolC<true>{}, BoolC<true>{}, it++);   // (lead > 0 implies ntiles > 1)
-  for (; it + 1 < ntiles; ++it) tile(BoolC<true>{}, BoolC<false>{}, it);
-  if (it < ntiles) tile(BoolC<false>{}, BoolC<false>{}, it);
+  if (lead > 32) tile(BoolC<true>{}, IntC<1>{}, it++);       // (lead > 0 implies ntiles > 1)
+  else if (lead > 0) tile(BoolC<true>{}, IntC<2>{}, it++);
+  for (; it + 1 < ntiles; ++it) tile(BoolC<true>{}, IntC<0>{}, it);
+  if (it < ntiles) tile(BoolC<false>{}, IntC<0>{}, it);
   wait_vmcnt<0>();   // copies queued for tiles that turned out empty
 
   const float l_tot = sum_xor32(sum_xor16(l_run));

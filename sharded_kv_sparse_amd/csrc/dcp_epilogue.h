@@ -344,6 +344,12 @@ struct WsPartial {
     if (half) store_coherent2(r, off, pack_f16x4(o * scale));
     else store_coherent4(r, off, o * scale);
   }
+  // The fp16 store without a branch (for a partial known to be fp16): when
+  // !keep it goes to an offset past the resource, where it is dropped.
+  __device__ void store_half(int d, const f32x4& o, bool keep) const {
+    const unsigned off = keep ? (unsigned)((d * nh + hl) * 4 + g) * 8u : 0x80000000u;
+    store_coherent2(r, off, pack_f16x4(o * scale));
+  }
 };
 
 // Writes this block's normalised partial (O / l and LSE = ln l + max) for
