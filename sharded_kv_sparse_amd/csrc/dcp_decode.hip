@@ -154,7 +154,8 @@ void decode_kernel(const DecodeParams p) {
     n_tok = min(p.counts[(long long)shard * p.rows + row], p.k);
   }
   n_tok = max(n_tok, 0);
-  const int chunk = ((n_tok + S - 1) / S + 63) / 64 * 64;
+  // splits of whole tiles (the last one takes the remainder)
+  const int chunk = ((n_tok + S - 1) / S + T - 1) / T * T;
   const int start = min(n_tok, split * chunk);
   const int end = min(n_tok, start + chunk);
   const int ntiles = (end - start + T - 1) / T;
