@@ -142,8 +142,10 @@ def fp8_kernel_mfma(p, w, splits):
     Per wave (16 heads) and 128-token tile: 8 S tiles x (4 latent k-steps x 2
     query terms + 1 RoPE k-step) + 32 dim tiles x 3 P' terms = 168; a tile of
     at most 64 valid tokens (the remainder past whole tiles) skips half the
-    S tiles and packs its P' terms into two MFMAs per dim tile: 100.  Every
-    MFMA is 16x16x128, 65,536 flops.  None for the other kernels."""
+    S tiles and packs its P' terms into two MFMAs per dim tile: 100; when
+    that remainder of at most 32 tokens leads a longer split, two S tiles
+    and one MFMA per dim tile: 50.  Every MFMA is 16x16x128, 65,536 flops.
+    None for the other kernels."""
     if p.kv_dtype != "fp8" or p.heads < 48:
         return None
     n_sh = p.num_shards
@@ -161,7 +163,8 @@ def fp8_kernel_mfma(p, w, splits):
             ln = max(0, min(int(n), (sp + 1) * chunk) - min(int(n), sp * chunk))
             tiles, rem = -(-ln // 128), ln % 128
             short = 1 if 0 < rem <= 64 else 0
-            per_wave += 168 * (tiles - short) + 100 * short
+            tiny = 1 if short and tiles > 1 and rem <= 32 else 0
+            per_wave += 168 * (tiles - short) + 100 * (short - tiny) + 50 * tiny
     return per_wave * 4 * -(-p.heads // 64)      # idle waves of a partial head block included
 
 
