@@ -66,6 +66,15 @@ __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
   int h = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, h, true);
 }
+// The same of four floats divided by a power of two `div` (the gfx950 scaled
+// conversion divides its inputs by its scale operand: for a power of two the
+// codes are those of the exact quotients, with no separate multiply).
+__device__ __forceinline__ int pack_e4m3_div(float a, float b, float c, float d, float div) {
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  s2 v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s2{0, 0}, a, b, div, false);
+  v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, c, d, div, true);
+  return __builtin_bit_cast(int, v);
+}
 
 // PARTIAL: the head count is not a multiple of 64 (the last head block has
 // idle waves).
@@ -603,15 +612,15 @@ void decode_fp8_kernel(const DecodeParams p) {
     // kb is taken from lane group kb, so every scale block spans two groups.
     pmax = max_xor32(max_xor16(pmax));
     const int ep = e4m3_exponent(pmax);
-    const float ps = pow2i(ep);
+    const float ps = pow2i(ep), ps_div = pow2i(-ep);
     const int pscale = 127 - ep;
     i32x8 pb[3] = {};                      // pb[term] byte 4st + i
 #pragma unroll
     for (int st = 0; st < NSS; ++st) {
-      float x[4];
+      float x[4];                          // (only in the residuals: fused there)
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = pr[st][i] * ps;
-      const int h = pack_e4m3(x[0], x[1], x[2], x[3]);
+      const int h = pack_e4m3_div(pr[st][0], pr[st][1], pr[st][2], pr[st][3], ps_div);
       const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
       const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
       const float r0 = x[0] - h01[0], r1 = x[1] - h01[1], r2 = x[2] - h23[0], r3 = x[3] - h23[1];
