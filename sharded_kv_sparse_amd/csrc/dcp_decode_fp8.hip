@@ -648,7 +648,7 @@ void decode_fp8_kernel(const DecodeParams p) {
       ex_ws = half_exponent(448.0f * max_xor32(max_xor16(smax)));
       pre_stored = ws_early;
     }
-    const WsPartial<kThreads, true> wsp(p, row, shard, split, head, g,
+    const WsPartial<kThreads, true, true> wsp(p, row, shard, split, head, g,
                                          l_fin > 0.f ? 1.0f / l_fin : 0.f, ex_ws);
     // No branch per store: the own dim tiles (kept in registers for the
     // merge) and an idle wave's tiles are stored past the end of the
@@ -740,7 +740,7 @@ void decode_fp8_kernel(const DecodeParams p) {
   wait_vmcnt<0>();   // copies queued for tiles that turned out empty
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
-  finish_block<kThreads, true>(p, row, shard, split, head, g, active, oacc, m_run * c, l_tot, smem, &s_flag,
+  finish_block<kThreads, true, true>(p, row, shard, split, head, g, active, oacc, m_run * c, l_tot, smem, &s_flag,
                                ex_ws, pre_stored);
 }
 

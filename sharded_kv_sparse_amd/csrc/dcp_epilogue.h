@@ -302,10 +302,11 @@ __device__ __forceinline__ int half_exponent(float bound) {
 constexpr int kExFromValues = -1000;         // finish_block: exponent from the values
 
 // Where and how a block's workspace partial is stored: fp16 scaled by
-// 2^-ex for the row merge, fp32 for the merge of one shard's splits; the
-// own dim tiles [od0, od1) of a block that merges its own part in parallel
-// stay in registers.  Element (d, head, lane group g) holds dims 16d + 4g..
-template <int NT, bool OWN>
+// 2^-ex for the row merge when HALF_X, else fp32 (always fp32 for the merge
+// of one shard's splits); the own dim tiles [od0, od1) of a block that
+// merges its own part in parallel stay in registers.  Element (d, head, lane
+// group g) holds dims 16d + 4g..
+template <int NT, bool OWN, bool HALF_X>
 struct WsPartial {
   bool half;
   int od0, od1, nh, hl, g, ex;
@@ -326,7 +327,7 @@ struct WsPartial {
     const bool own = OWN && may_wait && !need_shard_merge && n_in == 4 && nh * 4 == NT;
     od0 = own ? member * (32 / n_in) : 0;
     od1 = own ? od0 + 32 / n_in : 0;
-    half = fused && !need_shard_merge;
+    half = HALF_X && fused && !need_shard_merge;
     ex = half ? ex_ : 0;
     scale = half ? inv * pow2i(-ex) : inv;
     elem = half ? 8u : 16u;
@@ -364,7 +365,7 @@ struct WsPartial {
 // ex_given: the fp16 exponent when the caller has a bound (else it comes
 // from the values); pre_stored: the caller already stored the non-own dim
 // tiles of its workspace partial (with that exponent).
-template <int NT, bool OWN = false>
+template <int NT, bool OWN = false, bool HALF_X = false>
 __device__ __forceinline__ void finish_block(const DecodeParams& p, long long row, int shard, int split,
                                     int head, int g, bool writer, const f32x4 (&oacc)[32],
                                     float m_run, float l_tot, DCP_LDS char* smem, int* s_flag,
@@ -383,11 +384,14 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
   const long long blk_part = (row * N + shard) * S + split;
   const int n_in = N * S, member = shard * S + split;
   const bool may_wait = fused && p.merge_wait_ticks > 0 && n_in <= kMaxWaitMembers;
-  // The row merge exchanges fp16 partials (the merge of one shard's splits
-  // into o_part keeps fp32): each (partial, head) is scaled by a power of
-  // two 2^-ex that keeps every |value| below 2^15, so every value keeps 11
-  // significant bits (the merge weights carry the 2^ex back).
-  const bool half_ws = fused && !need_shard_merge;
+  // With HALF_X the row merge exchanges fp16 partials (the merge of one
+  // shard's splits into o_part keeps fp32): each (partial, head) is scaled
+  // by a power of two 2^-ex that keeps every |value| below 2^15, so every
+  // value keeps 11 significant bits (the merge weights carry the 2^ex back)
+  // and the merged O is within |O| * 2^-11 of the fp32 merge.  Without it
+  // (the generic kernel: more partials per row and a larger error of its
+  // own) the exchange is fp32.
+  const bool half_ws = HALF_X && fused && !need_shard_merge;
   int ex = 0;
   if (half_ws && writer) {
     if (ex_given != kExFromValues) {
@@ -401,7 +405,7 @@ __device__ __forceinline__ void finish_block(const DecodeParams& p, long long ro
       ex = half_exponent(max_xor32(max_xor16(amax * inv)));
     }
   }
-  const WsPartial<NT, OWN> wsp(p, row, shard, split, head, g, inv, ex);
+  const WsPartial<NT, OWN, HALF_X> wsp(p, row, shard, split, head, g, inv, ex);
   // Own part from registers: dim tiles [od0, od1) of this block's partial are
   // not stored unless the block gives its part up.
   const bool own = wsp.od1 > wsp.od0;

@@ -50,7 +50,7 @@ def draw_case(seed):
     return p, splits, want_partials, want_merged, out_dtype
 
 
-SEEDS = list(range(9001, 9049))
+SEEDS = list(range(9001, 9201))
 
 
 def test_random_cases_are_varied():
@@ -87,7 +87,7 @@ def test_random_configuration(gpu, seed):
     check_against_oracle(res, ref, f"random seed={seed}")
 
 
-PREFILL_SEEDS = list(range(9101, 9117))
+PREFILL_SEEDS = list(range(9101, 9151))
 
 
 @pytest.mark.gpu
