@@ -47,3 +47,18 @@ def test_fp8_kernel_mfma_hand_worked():
     p128 = SimpleNamespace(**{**vars(p), "heads": 128})
     assert bench.fp8_kernel_mfma(p128, w, 1) == 2 * 1744            # two 64-head blocks
     assert bench.fp8_kernel_mfma(SimpleNamespace(**{**vars(p), "kv_dtype": "bf16"}), w, 1) is None
+
+
+def test_fp8_kernel_mfma_lead_tiles():
+    # a remainder of at most 32 tokens ahead of a full tile is a "tiny" lead
+    # (two S tiles, one MFMA per dim tile: 18 + 32 = 50 per wave); 33..64
+    # ahead of one is a short lead (100); alone, any remainder up to 64 is a
+    # short tile (100)
+    from types import SimpleNamespace
+    p = SimpleNamespace(kv_dtype="fp8", heads=64, kind="sparse", num_shards=1, rows=3)
+    table = np.full((3, 256), -1, dtype=np.int64)
+    table[0, :150] = np.arange(150)       # 128 + 22: 168 + 50
+    table[1, :180] = np.arange(180)       # 128 + 52: 168 + 100
+    table[2, :20] = np.arange(20)         # 20 alone: 100
+    w = SimpleNamespace(table=table)
+    assert bench.fp8_kernel_mfma(p, w, 1) == 4 * (218 + 268 + 100)
