@@ -610,8 +610,10 @@ def test_kv_write_hand_worked_example(gpu, golden):
                                                ("dense", 64, 0), ("dense", 128, 0)])
 def test_fp8_lead_short_tile(gpu, kind, heads, splits):
     # rows whose token counts leave 1..64 tokens past whole 128-token tiles
-    # (the short tile then runs first), with 64 / 65 / whole-tile boundaries
-    lens = [129, 150, 192, 193, 256, 257, 320, 321, 449, 512]
+    # (the short tile then runs first: 1..32 tokens on the one-MFMA PV path,
+    # 33..64 on the two-MFMA one), with 32 / 33 / 64 / 65 / whole-tile
+    # boundaries
+    lens = [129, 150, 160, 161, 192, 193, 256, 257, 288, 289, 320, 321, 449, 512]
     if kind == "sparse":
         p = wl.Preset("t", "sparse", "fp8", batch=len(lens), q_per_seq=1, heads=heads, context=4000,
                       num_shards=1, topk=max(lens), seed=71 + heads)
